@@ -1,0 +1,88 @@
+"""Page-plan oracle: segments, true KV lengths, virtual pages and the physical map.
+
+Test infrastructure: see the package docstring. Pure Python integer code.
+
+Source: page "RedKnot SegPagedAttention runtime design", section 3 -- each (layer, head,
+segment) maps to contiguous virtual pages; the page table records, per head, the page numbers
+of its segments, its policy and its segment list; a shared physical pool where LOCAL heads
+allocate only sink + recent pages and GLOBAL heads the full context; a virtual-to-physical map
+keeps pages apart; the builder keeps only the tokens a LOCAL head can see. Section 4: the
+attention call reads each head's true KV length from its page table.
+
+Readings taken where the pages are silent (one layer per call):
+
+* A LOCAL head must store every token some query of the chunk can see. The chunk's queries
+  sit at positions L-q .. L-1, so the recent part starts at R0 = max(0, L - q - W + 1).
+* Segments, in position order: GLOBAL -> (0, L). LOCAL -> (0, L) when R0 <= S (sink and
+  window touch or overlap); else (R0, L - R0) when S = 0; else (0, S) and (R0, L - R0).
+  A sink longer than the context is clipped to L. L = 0 stores nothing.
+* Every segment starts on a fresh page; slot i of the segment's k-th page holds position
+  pos_start + k*P + i. n_pages = ceil(n_tok / P).
+* Virtual page ids are handed out in the order (request, head, segment); a segment's
+  vpage_start is the running total of the pages before it.
+* An unused segment slot reads (pos_start 0, n_tok 0, vpage_start = running total, n_pages 0).
+* v2p[v] = free_pages[v]: physical pages are taken from the caller's free list in order.
+* kv_len[b, h] = total stored tokens of the head.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+GLOBAL = 0
+LOCAL = 1
+
+
+def segments(kind: int, sink: int, window: int, L: int, q: int):
+    """List of (pos_start, n_tok) for one (request, KV head)."""
+    if L <= 0:
+        return []
+    if kind == GLOBAL:
+        return [(0, L)]
+    if kind != LOCAL:
+        raise ValueError(kind)
+    s = min(sink, L)
+    r0 = max(0, L - q - window + 1)
+    if r0 <= s:
+        return [(0, L)]
+    if s == 0:
+        return [(r0, L - r0)]
+    return [(0, s), (r0, L - r0)]
+
+
+def plan_tables(ctx_len, q_len, policy, P: int):
+    """Returns (seg_table int32 [B, Hkv, 2, 4], kv_len int32 [B, Hkv], n_virt)."""
+    B = len(ctx_len)
+    Hkv = len(policy)
+    seg_table = np.zeros((B, Hkv, 2, 4), dtype=np.int32)
+    kv_len = np.zeros((B, Hkv), dtype=np.int32)
+    v = 0
+    for b in range(B):
+        L = int(ctx_len[b])
+        q = int(q_len[b])
+        for h in range(Hkv):
+            kind, sink, window = (int(x) for x in policy[h])
+            segs = segments(kind, sink, window, L, q)
+            total = 0
+            for s in range(2):
+                if s < len(segs):
+                    pos, n = segs[s]
+                    npg = -(-n // P)
+                    seg_table[b, h, s] = (pos, n, v, npg)
+                    v += npg
+                    total += n
+                else:
+                    seg_table[b, h, s] = (0, 0, v, 0)
+            kv_len[b, h] = total
+    return seg_table, kv_len, v
+
+
+def gather_positions(seg_table, v2p, P: int, b: int, h: int):
+    """(position, physical page, slot) of every token stored for (b, h), in position order."""
+    out = []
+    for s in range(2):
+        pos, n, vstart, npg = (int(x) for x in seg_table[b, h, s])
+        for i in range(n):
+            vpage = vstart + i // P
+            out.append((pos + i, int(v2p[vpage]), i % P))
+    return out

@@ -1,0 +1,124 @@
+"""Pins for the page-plan oracle (CPU only).
+
+The plan's rules come from page "RedKnot SegPagedAttention runtime design", section 3. The
+pins: a hand-derived worked example (tests/golden/tiny_tables.json), closed-form page counts,
+page totals derived by hand for the 8K and 128K workloads, and -- tying storage to the
+visibility definition -- the stored positions of each head must be exactly the union of the
+positions its chunk's queries can see (built by brute force).
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import GLOBAL, LOCAL, gather_positions, plan_tables, segments
+from oracle import brute
+from workloads import config_case, free_list
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "tiny_tables.json")
+
+
+def test_tiny_worked_example():
+    g = json.load(open(GOLDEN))
+    seg, kv_len, n_virt = plan_tables(g["ctx_len"], g["q_len"], g["policy"], g["page_size"])
+    np.testing.assert_array_equal(seg, np.array(g["seg_table"], dtype=np.int32))
+    np.testing.assert_array_equal(kv_len, np.array(g["kv_len"], dtype=np.int32))
+    assert n_virt == g["n_virt"]
+
+
+@pytest.mark.parametrize("index,expected", [(0, 59), (1, 358), (4, 20136)])
+def test_page_totals_of_fixed_workloads(index, expected):
+    # 8K workload: 2 GLOBAL heads x 128 pages + 6 LOCAL heads x (1 + ceil(1023/64)) = 358.
+    # 128K workload: 8 x 2048 + 56 x (1 + ceil(4223/64)) = 20136.
+    c = config_case(index, with_tensors=False)
+    _, _, n_virt = plan_tables(c.ctx_len, c.q_len, c.policy, c.P)
+    assert n_virt == expected
+
+
+def _closed_form_pages(kind, S, W, L, q, P):
+    if L == 0:
+        return 0
+    if kind == GLOBAL:
+        return -(-L // P)
+    s = min(S, L)
+    r0 = max(0, L - q - W + 1)
+    if r0 <= s:
+        return -(-L // P)
+    return -(-s // P) + -(-(L - r0) // P)
+
+
+def test_page_counts_closed_form():
+    rng = np.random.default_rng(0)
+    for _ in range(400):
+        P = int(rng.choice([16, 32, 64]))
+        L = int(rng.integers(0, 300))
+        q = int(rng.integers(0, L + 1))
+        kind = int(rng.integers(0, 2))
+        S = int(rng.integers(0, 10))
+        W = int(rng.integers(1, 200))
+        seg, kv, n_virt = plan_tables([L], [q], [(kind, S, W)], P)
+        assert n_virt == _closed_form_pages(kind, S, W, L, q, P)
+        assert seg[0, 0, :, 3].sum() == n_virt
+        assert kv[0, 0] == seg[0, 0, :, 1].sum()
+
+
+def test_stored_set_is_union_of_visible_sets():
+    rng = np.random.default_rng(1)
+    for _ in range(300):
+        L = int(rng.integers(1, 120))
+        q = int(rng.integers(0, L + 1))
+        kind = int(rng.integers(0, 2))
+        S = int(rng.integers(0, 8))
+        W = int(rng.integers(1, 130))
+        stored = []
+        for pos, n in segments(kind, S, W, L, q):
+            stored.extend(range(pos, pos + n))
+        assert stored == sorted(set(stored)), "segments overlap or are out of order"
+        union = set()
+        for p in range(L - q, L):
+            union |= set(brute.visible_set(kind, S, W, p))
+        if q > 0:
+            assert set(stored) == union, (kind, S, W, L, q)
+
+
+def test_layout_invariants_and_gather():
+    c = config_case(0, with_tensors=False)
+    seg, kv_len, n_virt = plan_tables(c.ctx_len, c.q_len, c.policy, c.P)
+    fl = free_list(c.seed, n_virt + 5)
+    v2p = fl[:n_virt]
+    assert len(set(v2p.tolist())) == n_virt
+    # virtual pages are contiguous per segment and handed out in (b, h, seg) order
+    nxt = 0
+    for b in range(c.B):
+        for h in range(c.Hkv):
+            for s in range(2):
+                pos, n, vstart, npg = seg[b, h, s]
+                assert vstart == nxt
+                assert npg == -(-n // c.P)
+                nxt += npg
+    assert nxt == n_virt
+    # every stored position appears once, in a distinct (page, slot)
+    slots = set()
+    for b in range(c.B):
+        for h in range(c.Hkv):
+            rows = gather_positions(seg, v2p, c.P, b, h)
+            assert len(rows) == kv_len[b, h]
+            for pos, page, slot in rows:
+                assert (page, slot) not in slots
+                slots.add((page, slot))
+                assert 0 <= slot < c.P
+
+
+def test_empty_and_degenerate_heads():
+    assert segments(LOCAL, 4, 8, 0, 0) == []
+    assert segments(GLOBAL, 0, 1, 0, 0) == []
+    # sink longer than the context is clipped; window covering everything merges
+    assert segments(LOCAL, 50, 3, 10, 10) == [(0, 10)]
+    assert segments(LOCAL, 2, 100, 10, 1) == [(0, 10)]
+    assert segments(LOCAL, 0, 3, 10, 1) == [(7, 3)]
+    seg, kv, n = plan_tables([0, 5], [0, 2], [(LOCAL, 4, 2)], 16)
+    assert kv.tolist() == [[0], [5]]
+    assert seg[0, 0].tolist() == [[0, 0, 0, 0], [0, 0, 0, 0]]
+    assert seg[1, 0].tolist() == [[0, 5, 0, 1], [0, 0, 1, 0]]
