@@ -1,0 +1,29 @@
+"""Head-aware SegPaged attention for AMD Instinct MI355X (gfx950).
+
+The compute path is libsegpaged.so (HIP kernels behind the C ABI of include/segpaged.h);
+``binding`` exposes its calls under the same names and ``runtime`` owns the device buffers.
+"""
+
+from .binding import (  # noqa: F401
+    EXPORTED,
+    SP_BF16,
+    SP_F32,
+    SP_GLOBAL,
+    SP_LOCAL,
+    HipEvent,
+    SegPagedError,
+    lib,
+    segpaged_attention,
+    segpaged_attention_check,
+    segpaged_attention_plan,
+    segpaged_attention_profiled,
+    segpaged_attention_workspace_size,
+    segpaged_build,
+    segpaged_dense_mask_attention,
+    segpaged_dense_mask_plan,
+    segpaged_dense_mask_workspace_size,
+    segpaged_layout_tables,
+    segpaged_plan_pages,
+    status_string,
+)
+from .runtime import DenseMaskLayer, SegPagedLayer  # noqa: F401

@@ -1,0 +1,360 @@
+// C ABI of libsegpaged (declared in include/segpaged.h): argument validation, table uploads
+// and kernel launches. Every argument is checked before anything is queued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "launch.h"
+#include "planner.h"
+#include "segpaged.h"
+
+using namespace sp;
+
+namespace {
+
+sp_status device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SP_ERR_HIP;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return SP_ERR_HIP;
+  *cus = n > 0 ? n : 1;
+  return SP_OK;
+}
+
+// Persistent grid sizes for one shape: resident work groups of each kernel.
+sp_status grids(const Shape& s, int32_t* g_pre, int32_t* g_dec) {
+  int cus = 0;
+  sp_status st = device_cus(&cus);
+  if (st != SP_OK) return st;
+  *g_pre = cus * attention_occupancy(s.dtype, s.D, s.mode, false);
+  *g_dec = cus * attention_occupancy(s.dtype, s.D, s.mode, true);
+  return SP_OK;
+}
+
+Shape make_shape(int32_t mode, sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                 int32_t P, const int32_t* ctx_len, const int32_t* q_len,
+                 const sp_head_policy* pol) {
+  Shape s;
+  s.mode = mode;
+  s.dtype = int32_t(dtype);
+  s.B = B;
+  s.Hq = Hq;
+  s.Hkv = Hkv;
+  s.D = D;
+  s.P = mode == kModePaged ? P : 64;
+  s.ctx_len = ctx_len;
+  s.q_len = q_len;
+  s.pol = pol;
+  return s;
+}
+
+sp_status workspace_size(const Shape& s, size_t* bytes) {
+  if (bytes == nullptr) return SP_ERR_INVALID_ARG;
+  sp_status st = check_shape(s);
+  if (st != SP_OK) return st;
+  int32_t gp = 0, gd = 0;
+  st = grids(s, &gp, &gd);
+  if (st != SP_OK) return st;
+  Plan plan;
+  st = make_plan(s, gp, gd, &plan);
+  if (st != SP_OK) return st;
+  *bytes = plan.bytes;
+  return SP_OK;
+}
+
+sp_status plan_into(const Shape& s, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  sp_status st = check_shape(s);
+  if (st != SP_OK) return st;
+  if (workspace == nullptr) return SP_ERR_INVALID_ARG;
+  int32_t gp = 0, gd = 0;
+  st = grids(s, &gp, &gd);
+  if (st != SP_OK) return st;
+  Plan plan;
+  st = make_plan(s, gp, gd, &plan);
+  if (st != SP_OK) return st;
+  if (ws_bytes < plan.bytes) return SP_ERR_WORKSPACE_TOO_SMALL;
+  std::vector<uint8_t> buf;
+  serialize_plan(plan, &buf);
+  if (hipMemcpyAsync(workspace, buf.data(), buf.size(), hipMemcpyHostToDevice, stream) !=
+      hipSuccess)
+    return SP_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SP_ERR_HIP;
+  return SP_OK;
+}
+
+sp_status run_attention(const Shape& s, const void* q, const void* k, const void* v,
+                        int64_t n_phys, const int32_t* seg_table, const int32_t* kv_len,
+                        const int32_t* v2p, float scale, void* o, void* workspace,
+                        size_t ws_bytes, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  sp_status st = check_shape(s);
+  if (st != SP_OK) return st;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return SP_ERR_INVALID_ARG;
+  bool need_pre = false, need_dec = false;
+  needed_kernels(s, &need_pre, &need_dec);
+  if (!need_pre && !need_dec) {
+    if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return SP_ERR_HIP;
+    if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return SP_ERR_HIP;
+    return SP_OK;
+  }
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || workspace == nullptr)
+    return SP_ERR_INVALID_ARG;
+  if (s.mode == kModePaged &&
+      (seg_table == nullptr || kv_len == nullptr || v2p == nullptr || n_phys < 1))
+    return SP_ERR_INVALID_ARG;
+  if (ws_bytes < size_t(kHeaderBytes)) return SP_ERR_WORKSPACE_TOO_SMALL;
+  int32_t gp = 0, gd = 0;
+  st = grids(s, &gp, &gd);
+  if (st != SP_OK) return st;
+
+  AttnParams p;
+  p.q = q;
+  p.o = o;
+  p.k = k;
+  p.v = v;
+  p.seg_table = seg_table;
+  p.kv_len = kv_len;
+  p.v2p = v2p;
+  p.n_phys = n_phys;
+  p.ws = static_cast<uint8_t*>(workspace);
+  p.signature = shape_signature(s, gp, gd);
+  p.ws_bytes = ws_bytes;
+  p.Hq = s.Hq;
+  p.Hkv = s.Hkv;
+  p.G = s.Hq / s.Hkv;
+  p.P = s.P;
+  p.scale_log2 = scale * 1.4426950408889634f;
+
+  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return SP_ERR_HIP;
+  if (need_pre && launch_attention(s.dtype, s.D, s.mode, false, gp, p, stream) != hipSuccess)
+    return SP_ERR_HIP;
+  if (need_dec && launch_attention(s.dtype, s.D, s.mode, true, gd, p, stream) != hipSuccess)
+    return SP_ERR_HIP;
+  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return SP_ERR_HIP;
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != SP_OK) return st;
+  if (launch_combine(s.dtype, s.D, 2 * cus, p, stream) != hipSuccess) return SP_ERR_HIP;
+  return SP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* segpaged_status_string(int status) {
+  switch (status) {
+    case SP_OK: return "SP_OK";
+    case SP_ERR_INVALID_ARG: return "SP_ERR_INVALID_ARG: invalid argument";
+    case SP_ERR_UNSUPPORTED: return "SP_ERR_UNSUPPORTED: unsupported shape, dtype or size";
+    case SP_ERR_POOL_TOO_SMALL: return "SP_ERR_POOL_TOO_SMALL: free list shorter than needed";
+    case SP_ERR_WORKSPACE_TOO_SMALL: return "SP_ERR_WORKSPACE_TOO_SMALL: workspace too small";
+    case SP_ERR_HIP: return "SP_ERR_HIP: HIP runtime error";
+    case SP_ERR_PLAN_MISMATCH: return "SP_ERR_PLAN_MISMATCH: workspace planned for other arguments";
+    default: return "unknown status";
+  }
+}
+
+sp_status segpaged_plan_pages(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                              int32_t Hkv, const sp_head_policy* pol, int32_t page_size,
+                              int64_t* n_pages_needed) {
+  if (n_pages_needed == nullptr) return SP_ERR_INVALID_ARG;
+  sp_status st = check_page_size(page_size);
+  if (st != SP_OK) return st;
+  st = check_lengths_policy(B, ctx_len, q_len, Hkv, pol);
+  if (st != SP_OK) return st;
+  Layout lay;
+  st = make_layout(B, ctx_len, q_len, Hkv, pol, page_size, &lay);
+  if (st != SP_OK) return st;
+  *n_pages_needed = lay.n_virt;
+  return SP_OK;
+}
+
+sp_status segpaged_layout_tables(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                                int32_t Hkv, const sp_head_policy* pol, int32_t page_size,
+                                int32_t* seg_table, int32_t* kv_len) {
+  if (seg_table == nullptr || kv_len == nullptr) return SP_ERR_INVALID_ARG;
+  sp_status st = check_page_size(page_size);
+  if (st != SP_OK) return st;
+  st = check_lengths_policy(B, ctx_len, q_len, Hkv, pol);
+  if (st != SP_OK) return st;
+  Layout lay;
+  st = make_layout(B, ctx_len, q_len, Hkv, pol, page_size, &lay);
+  if (st != SP_OK) return st;
+  layout_tables(lay, B, Hkv, seg_table, kv_len);
+  return SP_OK;
+}
+
+sp_status segpaged_build(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int32_t page_size,
+                         const int32_t* ctx_len, const int32_t* q_len, const sp_head_policy* pol,
+                         const void* k_dense, const void* v_dense, const int32_t* free_pages,
+                         int64_t n_free, int64_t n_phys, void* k_pool, void* v_pool,
+                         int32_t* seg_table, int32_t* kv_len, int32_t* v2p, hipStream_t stream) {
+  sp_status st = check_dtype_dim(dtype, D);
+  if (st != SP_OK) return st;
+  st = check_page_size(page_size);
+  if (st != SP_OK) return st;
+  st = check_lengths_policy(B, ctx_len, q_len, Hkv, pol);
+  if (st != SP_OK) return st;
+  if (n_free < 0 || n_phys < 0) return SP_ERR_INVALID_ARG;
+  Layout lay;
+  st = make_layout(B, ctx_len, q_len, Hkv, pol, page_size, &lay);
+  if (st != SP_OK) return st;
+  if (B == 0) return SP_OK;
+  if (seg_table == nullptr || kv_len == nullptr) return SP_ERR_INVALID_ARG;
+  const int64_t n_virt = lay.n_virt;
+  if (n_free < n_virt) return SP_ERR_POOL_TOO_SMALL;
+  if (n_virt > 0) {
+    if (free_pages == nullptr || v2p == nullptr || k_pool == nullptr || v_pool == nullptr ||
+        k_dense == nullptr || v_dense == nullptr)
+      return SP_ERR_INVALID_ARG;
+    std::vector<uint8_t> seen(size_t(n_phys), 0);
+    for (int64_t i = 0; i < n_virt; ++i) {
+      const int32_t f = free_pages[i];
+      if (f < 0 || f >= n_phys || seen[size_t(f)]) return SP_ERR_INVALID_ARG;
+      seen[size_t(f)] = 1;
+    }
+  }
+  std::vector<int32_t> tab(size_t(B) * Hkv * 8), kl(size_t(B) * Hkv);
+  layout_tables(lay, B, Hkv, tab.data(), kl.data());
+  if (hipMemcpyAsync(seg_table, tab.data(), tab.size() * 4, hipMemcpyHostToDevice, stream) !=
+          hipSuccess ||
+      hipMemcpyAsync(kv_len, kl.data(), kl.size() * 4, hipMemcpyHostToDevice, stream) !=
+          hipSuccess)
+    return SP_ERR_HIP;
+  if (n_virt > 0 && hipMemcpyAsync(v2p, free_pages, size_t(n_virt) * 4, hipMemcpyHostToDevice,
+                                   stream) != hipSuccess)
+    return SP_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SP_ERR_HIP;
+
+  // Scatter: one launch per run of at most kMaxBuildSegs non-empty segments.
+  BuildParams bp;
+  std::memset(&bp, 0, sizeof(bp));
+  bp.k = k_dense;
+  bp.v = v_dense;
+  bp.kp = k_pool;
+  bp.vp = v_pool;
+  bp.v2p = v2p;
+  bp.Hkv = Hkv;
+  bp.P = page_size;
+  int64_t row0 = 0;
+  auto flush = [&]() -> sp_status {
+    if (bp.nseg == 0) return SP_OK;
+    if (launch_build(dtype, D, bp, stream) != hipSuccess) return SP_ERR_HIP;
+    bp.nseg = 0;
+    bp.nchunks = 0;
+    return SP_OK;
+  };
+  for (int32_t b = 0; b < B; ++b) {
+    for (int32_t h = 0; h < Hkv; ++h) {
+      const HeadLayout& hl = lay.heads[size_t(b) * Hkv + h];
+      for (int s = 0; s < hl.nseg; ++s) {
+        const Segment& sg = hl.seg[s];
+        if (sg.ntok == 0) continue;
+        if (bp.nseg == kMaxBuildSegs) {
+          st = flush();
+          if (st != SP_OK) return st;
+        }
+        BuildSeg& e = bp.seg[bp.nseg++];
+        e.chunk0 = bp.nchunks;
+        e.src_row0 = int32_t(row0 + sg.pos);
+        e.vstart = sg.vstart;
+        e.ntok = sg.ntok;
+        e.h = h;
+        bp.nchunks += (sg.ntok + kChunk - 1) / kChunk;
+      }
+    }
+    row0 += ctx_len[b];
+  }
+  return flush();
+}
+
+sp_status segpaged_attention_workspace_size(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                            int32_t D, int32_t page_size,
+                                            const int32_t* ctx_len, const int32_t* q_len,
+                                            const sp_head_policy* pol, size_t* bytes) {
+  return workspace_size(
+      make_shape(kModePaged, dtype, B, Hq, Hkv, D, page_size, ctx_len, q_len, pol), bytes);
+}
+
+sp_status segpaged_attention_plan(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t page_size, const int32_t* ctx_len,
+                                  const int32_t* q_len, const sp_head_policy* pol,
+                                  void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return plan_into(make_shape(kModePaged, dtype, B, Hq, Hkv, D, page_size, ctx_len, q_len, pol),
+                   workspace, ws_bytes, stream);
+}
+
+sp_status segpaged_attention(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                             int32_t page_size, const int32_t* ctx_len, const int32_t* q_len,
+                             const sp_head_policy* pol, const void* q, const void* k_pool,
+                             const void* v_pool, int64_t n_phys, const int32_t* seg_table,
+                             const int32_t* kv_len, const int32_t* v2p, float softmax_scale,
+                             void* o, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return run_attention(
+      make_shape(kModePaged, dtype, B, Hq, Hkv, D, page_size, ctx_len, q_len, pol), q, k_pool,
+      v_pool, n_phys, seg_table, kv_len, v2p, softmax_scale, o, workspace, ws_bytes, stream,
+      nullptr, nullptr);
+}
+
+sp_status segpaged_attention_profiled(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                      int32_t D, int32_t page_size, const int32_t* ctx_len,
+                                      const int32_t* q_len, const sp_head_policy* pol,
+                                      const void* q, const void* k_pool, const void* v_pool,
+                                      int64_t n_phys, const int32_t* seg_table,
+                                      const int32_t* kv_len, const int32_t* v2p,
+                                      float softmax_scale, void* o, void* workspace,
+                                      size_t ws_bytes, hipStream_t stream,
+                                      hipEvent_t main_begin, hipEvent_t main_end) {
+  return run_attention(
+      make_shape(kModePaged, dtype, B, Hq, Hkv, D, page_size, ctx_len, q_len, pol), q, k_pool,
+      v_pool, n_phys, seg_table, kv_len, v2p, softmax_scale, o, workspace, ws_bytes, stream,
+      main_begin, main_end);
+}
+
+sp_status segpaged_attention_check(void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (workspace == nullptr || ws_bytes < size_t(kHeaderBytes)) return SP_ERR_INVALID_ARG;
+  int32_t word = 0;
+  uint8_t* w = static_cast<uint8_t*>(workspace) + kOffError;
+  if (hipMemcpyAsync(&word, w, 4, hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return SP_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SP_ERR_HIP;
+  if (word != 0) {
+    const int32_t zero = 0;
+    if (hipMemcpyAsync(w, &zero, 4, hipMemcpyHostToDevice, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      return SP_ERR_HIP;
+  }
+  return sp_status(word);
+}
+
+sp_status segpaged_dense_mask_workspace_size(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                             int32_t D, const int32_t* ctx_len,
+                                             const int32_t* q_len, const sp_head_policy* pol,
+                                             size_t* bytes) {
+  return workspace_size(make_shape(kModeDense, dtype, B, Hq, Hkv, D, 64, ctx_len, q_len, pol),
+                        bytes);
+}
+
+sp_status segpaged_dense_mask_plan(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                   const int32_t* ctx_len, const int32_t* q_len,
+                                   const sp_head_policy* pol, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream) {
+  return plan_into(make_shape(kModeDense, dtype, B, Hq, Hkv, D, 64, ctx_len, q_len, pol),
+                   workspace, ws_bytes, stream);
+}
+
+sp_status segpaged_dense_mask_attention(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                        int32_t D, const int32_t* ctx_len, const int32_t* q_len,
+                                        const sp_head_policy* pol, const void* q,
+                                        const void* k_dense, const void* v_dense,
+                                        float softmax_scale, void* o, void* workspace,
+                                        size_t ws_bytes, hipStream_t stream) {
+  return run_attention(make_shape(kModeDense, dtype, B, Hq, Hkv, D, 64, ctx_len, q_len, pol), q,
+                       k_dense, v_dense, 0, nullptr, nullptr, nullptr, softmax_scale, o,
+                       workspace, ws_bytes, stream, nullptr, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,958 @@
+// HIP kernels of libsegpaged for CDNA4 (gfx950): build/scatter, varlen prefill attention,
+// split-KV decode attention and the fixed-order cross-split combine.
+//
+// Method: page "RedKnot SegPagedAttention runtime design", sections 3-4. Each (request, KV
+// head) walks only its own stored tokens through its page table; GLOBAL heads walk the whole
+// prefix, LOCAL heads the sink and the recent window. All (query head, KV head) pairs of a
+// batch run in one persistent launch that pops work items from per-XCD queues.
+//
+// Data layout in the kernels:
+// - One KV step = 64 stored tokens of one segment (64-aligned in the segment), staged in LDS
+//   as K [64][D + pad] (row-major) and V^T [D][64 + pad] (transposed while storing, so that
+//   the P*V contraction reads 8 consecutive keys per lane), double-buffered, with the next
+//   step's global loads in flight in registers while the current step is computed.
+// - Prefill tile: 128 rows = (query token, query head of the GQA group) pairs of one KV
+//   head; wave w owns rows 32w..32w+31. S^T = K * Q^T on 32x32 MFMA puts one query row per
+//   lane column, so the softmax row statistics are per lane (plus one cross-half exchange)
+//   and the O^T accumulators are rescaled in-lane.
+// - Decode item: up to 16 rows; wave w takes keys 16w..16w+15 of each step on 16x16 MFMA and
+//   keeps its own running (m, l, O); the four waves merge through LDS at the end.
+// Softmax runs in base 2 with scale*log2(e) folded into one FMA; masks are evaluated only on
+// steps that straddle a visibility edge or are not full.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "segpaged.h"
+
+namespace sp {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+
+struct BF16 {
+  using S = uint16_t;
+  static constexpr int kVec = 8;  // elements per 16-byte access
+  static constexpr int KPL = 8;   // reduction elements per lane of one MFMA
+  using Frag = bf16x8_t;
+};
+
+struct F32 {
+  using S = float;
+  static constexpr int kVec = 4;
+  static constexpr int KPL = 1;
+  using Frag = float;
+};
+
+__device__ __forceinline__ f32x16_t mma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mma32(float a, float b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma16(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <class E>
+__device__ __forceinline__ typename E::Frag load_frag(const typename E::S* p) {
+  if constexpr (E::KPL == 8) {
+    return *reinterpret_cast<const bf16x8_t*>(p);
+  } else {
+    return *p;
+  }
+}
+
+template <class E>
+__device__ __forceinline__ typename E::Frag zero_frag() {
+  if constexpr (E::KPL == 8) {
+    u32x4_t z = {0u, 0u, 0u, 0u};
+    return __builtin_bit_cast(bf16x8_t, z);
+  } else {
+    return 0.f;
+  }
+}
+
+__device__ __forceinline__ bf16x8_t to_bf16x8(float a0, float a1, float a2, float a3, float a4,
+                                              float a5, float a6, float a7) {
+  f32x8_t f = {a0, a1, a2, a3, a4, a5, a6, a7};
+  return __builtin_convertvector(f, bf16x8_t);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Slot of key kv (0..63) in a V^T row. Prefill (32x32 MFMA): the S^T accumulator register r
+// of lane half hh holds key 8*(r/4) + 4*hh + r%4 of a 32-key block; keys feeding one P*V MFMA
+// are stored side by side so each lane reads them with one access. Decode (16x16 MFMA):
+// lane quad k4 holds keys 4*k4 .. 4*k4+3, the natural order.
+template <int KPL, bool kPrefill>
+__device__ __forceinline__ int vt_slot(int kv) {
+  if constexpr (!kPrefill) {
+    return kv;
+  } else {
+    const int kb = kv >> 5, kl = kv & 31;
+    const int hh = (kl >> 2) & 1;
+    const int r = 4 * (kl >> 3) + (kl & 3);
+    return 32 * kb + (2 * (r / KPL) + hh) * KPL + (r % KPL);
+  }
+}
+
+__device__ __forceinline__ void set_error(uint8_t* ws, int code) {
+  atomicCAS(reinterpret_cast<int*>(ws + kOffError), 0, code);
+}
+
+// Pops the next work item: own XCD's queue first, then the others. Thread 0 only.
+__device__ __forceinline__ int pop_item(uint8_t* ws, const int32_t* qb, int cnt_off, int xcd,
+                                        uint32_t& exhausted) {
+  for (int k = 0; k < kXcds; ++k) {
+    const int x = (xcd + k) & (kXcds - 1);
+    if (exhausted & (1u << x)) continue;
+    const int n = qb[x + 1] - qb[x];
+    if (n > 0) {
+      const int t = atomicAdd(reinterpret_cast<int*>(ws + cnt_off + x * 128), 1);
+      if (t < n) return qb[x] + t;
+    }
+    exhausted |= 1u << x;
+  }
+  return -1;
+}
+
+// The last work group to finish returns the queue counters to zero for the next launch.
+__device__ __forceinline__ void retire(uint8_t* ws, int cnt_off, int done_off) {
+  const int d = atomicAdd(reinterpret_cast<int*>(ws + done_off), 1);
+  if (d == int(gridDim.x) - 1) {
+    for (int x = 0; x < kXcds; ++x) atomicExch(reinterpret_cast<int*>(ws + cnt_off + x * 128), 0);
+    atomicExch(reinterpret_cast<int*>(ws + done_off), 0);
+  }
+}
+
+// Per-item view of the KV source: segment table of (b, h) and the step list.
+struct ItemKV {
+  int pos0, ntok0, vstart0;
+  int pos1, ntok1, vstart1;
+  int n_ra;
+};
+
+struct Step {
+  int seg, ti0, vlo, vhi, pos0;
+};
+
+__device__ __forceinline__ Step describe_step(const WorkItem& w, const ItemKV& kv, int c,
+                                              bool dense) {
+  Step s;
+  int base, lo, hi;
+  if (c < kv.n_ra) {
+    s.seg = w.ra_seg;
+    base = w.ra_begin / kChunk + c;
+    lo = w.ra_begin;
+    hi = w.ra_end;
+  } else {
+    s.seg = w.rb_seg;
+    base = w.rb_begin / kChunk + (c - kv.n_ra);
+    lo = w.rb_begin;
+    hi = w.rb_end;
+  }
+  s.ti0 = base * kChunk;
+  s.vlo = max(0, lo - s.ti0);
+  s.vhi = min(kChunk, hi - s.ti0);
+  s.pos0 = dense ? s.ti0 : (s.seg == 0 ? kv.pos0 : kv.pos1) + s.ti0;
+  return s;
+}
+
+// ---------------------------------------------------------------------------------------
+// KV step loader: global -> registers (issued one step ahead) -> LDS.
+// ---------------------------------------------------------------------------------------
+template <class E, int D, bool kPrefill>
+struct KVLoader {
+  using S = typename E::S;
+  static constexpr int kVec = E::kVec;
+  static constexpr int kColsPerRow = D / kVec;              // 16-byte pieces per row
+  static constexpr int kKLoads = (kChunk * kColsPerRow) / 256;
+  static constexpr int kVUnits = 16 * kColsPerRow;          // (4 keys x kVec dims) units
+  static constexpr int kVLoads = (kVUnits + 255) / 256;
+  static constexpr int KS = D + kVec;                       // K row stride (elements)
+  static constexpr int VS = kChunk + kVec;                  // V^T row stride (elements)
+  static constexpr int kKElems = kChunk * KS;
+  static constexpr int kVElems = D * VS;
+  static constexpr uint32_t kOut = 0x80000000u;             // offset past num_records: reads 0
+
+  u32x4_t kr[kKLoads];
+  u32x4_t vr[kVLoads][4];
+
+  // V unit u of this thread: 4 consecutive keys 4*rg .. 4*rg+3 and dims dc*kVec ...
+  __device__ __forceinline__ static void v_unit(int u, int& rg, int& dc) {
+    rg = u % 16;
+    dc = u / 16;
+  }
+
+  // Byte offset of (row, piece col) of the step inside the buffer that starts at `base`.
+  // Loads go through buffer descriptors rebased per step, so every offset is 32-bit and rows
+  // outside the step's valid window read as zero (offset beyond num_records).
+  __device__ __forceinline__ void load(const AttnParams& p, const WorkItem& w, const ItemKV& kv,
+                                       const Step& st, bool dense, uint8_t* ws) {
+    const int tid = threadIdx.x;
+    const S* kbase = static_cast<const S*>(p.k);
+    const S* vbase = static_cast<const S*>(p.v);
+    int64_t off = 0;       // element offset of the descriptor base
+    uint32_t rs = 0;       // row stride in bytes (uniform cases)
+    bool per_row = false;  // small pages: each row looks up its own page
+    int vs = 0;
+    bool uni_ok = true;
+    if (dense) {
+      off = (int64_t(w.kv_row0 + st.ti0) * p.Hkv + w.h) * D;
+      rs = uint32_t(p.Hkv) * D * sizeof(S);
+    } else {
+      vs = st.seg == 0 ? kv.vstart0 : kv.vstart1;
+      if (p.P >= kChunk) {
+        int phys = uniform(p.v2p[vs + st.ti0 / p.P]);
+        if (uint32_t(phys) >= uint64_t(p.n_phys)) {
+          uni_ok = false;
+          phys = 0;
+          if (tid == 0) set_error(ws, SP_ERR_INVALID_ARG);
+        }
+        off = (int64_t(phys) * p.P + (st.ti0 & (p.P - 1))) * D;
+        rs = D * sizeof(S);
+      } else {
+        per_row = true;
+      }
+    }
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), (short)0, 0x7fffffff, 0x00020000);
+    auto row_off = [&](int row) -> uint32_t {
+      if (!uni_ok || row < st.vlo || row >= st.vhi) return kOut;
+      if (!per_row) return uint32_t(row) * rs;
+      const int ti = st.ti0 + row;
+      const int phys = p.v2p[vs + ti / p.P];
+      if (uint32_t(phys) >= uint64_t(p.n_phys)) return kOut;
+      return uint32_t((phys * p.P + (ti & (p.P - 1))) * D * int(sizeof(S)));
+    };
+#pragma unroll
+    for (int j = 0; j < kKLoads; ++j) {
+      const int idx = tid + 256 * j;
+      const int row = idx / kColsPerRow, col = idx % kColsPerRow;
+      const uint32_t o = row_off(row);
+      kr[j] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o == kOut ? o : o + col * 16, 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < kVLoads; ++j) {
+      int rg, dc;
+      v_unit(tid + 256 * j, rg, dc);
+      const bool unit_ok = tid + 256 * j < kVUnits;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t o = unit_ok ? row_off(4 * rg + e) : kOut;
+        vr[j][e] = __builtin_bit_cast(
+            u32x4_t,
+            __builtin_amdgcn_raw_buffer_load_b128(rv, o == kOut ? o : o + dc * 16, 0, 0));
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(S* lk, S* lv) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < kKLoads; ++j) {
+      const int idx = tid + 256 * j;
+      const int row = idx / kColsPerRow, col = idx % kColsPerRow;
+      *reinterpret_cast<u32x4_t*>(lk + row * KS + col * kVec) = kr[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kVLoads; ++j) {
+      if (tid + 256 * j >= kVUnits) continue;
+      int rg, dc;
+      v_unit(tid + 256 * j, rg, dc);
+      if constexpr (E::KPL == 8) {
+        // 4 keys x 8 dims -> 8 V^T rows of 4 consecutive slots (8 bytes each).
+        const int slot0 = vt_slot<8, kPrefill>(4 * rg);
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+          const int wd = dd >> 1;
+          const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+          u32x2_t o;
+          o[0] = __builtin_amdgcn_perm(vr[j][1][wd], vr[j][0][wd], sel);
+          o[1] = __builtin_amdgcn_perm(vr[j][3][wd], vr[j][2][wd], sel);
+          *reinterpret_cast<u32x2_t*>(lv + (dc * 8 + dd) * VS + slot0) = o;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int slot = vt_slot<1, kPrefill>(4 * rg + e);
+#pragma unroll
+          for (int dd = 0; dd < 4; ++dd) {
+            lv[(dc * 4 + dd) * VS + slot] = __builtin_bit_cast(float, vr[j][e][dd]);
+          }
+        }
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ void load_item_kv(const AttnParams& p, const WorkItem& w, bool dense,
+                                             ItemKV& kv, uint8_t* ws) {
+  if (!dense) {
+    const int32_t* e = p.seg_table + (int64_t(w.b) * p.Hkv + w.h) * 8;
+    kv.pos0 = uniform(e[0]);
+    kv.ntok0 = uniform(e[1]);
+    kv.vstart0 = uniform(e[2]);
+    kv.pos1 = uniform(e[4]);
+    kv.ntok1 = uniform(e[5]);
+    kv.vstart1 = uniform(e[6]);
+    const int kl = uniform(p.kv_len[int64_t(w.b) * p.Hkv + w.h]);
+    const int na = w.ra_seg == 0 ? kv.ntok0 : kv.ntok1;
+    const int nb = w.rb_seg == 0 ? kv.ntok0 : kv.ntok1;
+    const bool bad = kl != kv.ntok0 + kv.ntok1 || (w.ra_end > w.ra_begin && w.ra_end > na) ||
+                     (w.rb_end > w.rb_begin && w.rb_end > nb);
+    if (bad && threadIdx.x == 0) set_error(ws, SP_ERR_INVALID_ARG);
+  } else {
+    kv.pos0 = kv.pos1 = 0;
+    kv.ntok0 = kv.ntok1 = 0;
+    kv.vstart0 = kv.vstart1 = 0;
+  }
+  kv.n_ra = w.ra_end > w.ra_begin ? (w.ra_end + kChunk - 1) / kChunk - w.ra_begin / kChunk : 0;
+}
+
+__device__ __forceinline__ WorkItem load_item(const WorkItem* items, int it) {
+  const int32_t* src = reinterpret_cast<const int32_t*>(items + it);
+  WorkItem w;
+  int32_t* dst = reinterpret_cast<int32_t*>(&w);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dst[i] = uniform(src[i]);
+  return w;
+}
+
+__device__ __forceinline__ bool header_ok(const AttnParams& p) {
+  const WsHeader* hd = reinterpret_cast<const WsHeader*>(p.ws);
+  return hd->magic == kMagic && hd->signature == p.signature && hd->bytes <= p.ws_bytes;
+}
+
+// ---------------------------------------------------------------------------------------
+// Prefill: persistent, 256 threads, 128-row tiles.
+// ---------------------------------------------------------------------------------------
+template <class E, int D, int MODE>
+__global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
+    prefill_kernel(AttnParams p) {
+  using S = typename E::S;
+  using L = KVLoader<E, D, true>;
+  constexpr int KPL = E::KPL;
+  constexpr int NQK = D / (2 * KPL);   // MFMAs per 32-key block for S^T = K Q^T
+  constexpr int NPV = 16 / KPL;        // MFMAs per 32-key block and 32-dim block for P V
+  constexpr int ND = D / 32;           // 32-dim blocks of O^T
+  constexpr bool kDense = MODE == kModeDense;
+
+  __shared__ __attribute__((aligned(16))) S lds_k[2][L::kKElems];
+  __shared__ __attribute__((aligned(16))) S lds_v[2][L::kVElems];
+  __shared__ int s_item;
+
+  if (!header_ok(p)) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) set_error(p.ws, SP_ERR_PLAN_MISMATCH);
+    return;
+  }
+  const WsHeader* hd = reinterpret_cast<const WsHeader*>(p.ws);
+  const WorkItem* items = reinterpret_cast<const WorkItem*>(p.ws + hd->off_prefill);
+  const int32_t* pol = reinterpret_cast<const int32_t*>(p.ws + hd->off_policy);
+  float* part_o = reinterpret_cast<float*>(p.ws + hd->off_part_pre);
+  float* part_ml = reinterpret_cast<float*>(p.ws + hd->off_ml_pre);
+
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int lq = lane & 31, hh = lane >> 5;
+  const int xcd = blockIdx.x % kXcds;
+  uint32_t exhausted = 0;
+  const S* qbase = static_cast<const S*>(p.q);
+  S* obase = static_cast<S*>(p.o);
+
+  for (;;) {
+    if (tid == 0) s_item = pop_item(p.ws, hd->prefill_q, kOffPrefillCnt, xcd, exhausted);
+    __syncthreads();
+    const int it = uniform(s_item);
+    if (it < 0) break;
+    const WorkItem w = load_item(items, it);
+    ItemKV kv;
+    load_item_kv(p, w, kDense, kv, p.ws);
+    const int kind = uniform(pol[w.h * 3 + 0]);
+    const int sink = uniform(pol[w.h * 3 + 1]);
+    const int window = uniform(pol[w.h * 3 + 2]);
+
+    // This lane's query row.
+    const int r = wave * 32 + lq;
+    const int tl = r / p.G, g = r - tl * p.G;
+    const bool row_ok = tl < w.nq;
+    const int p_row = w.p0 + w.tq0 + tl;
+    const int64_t orow = int64_t(w.q_row0 + w.tq0 + tl) * p.Hq + int64_t(w.h) * p.G + g;
+    typename E::Frag qf[NQK];
+#pragma unroll
+    for (int c = 0; c < NQK; ++c) {
+      qf[c] = row_ok ? load_frag<E>(qbase + orow * D + 2 * KPL * c + KPL * hh) : zero_frag<E>();
+    }
+    const int pmin = w.p0 + w.tq0, pmax = pmin + w.nq - 1;
+
+    f32x16_t oacc[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) oacc[d] = f32x16_t{};
+    float m_run = kNegInf, l_run = 0.f;
+
+    L ld;
+    const int n = w.c_end - w.c_begin;
+    Step cur = describe_step(w, kv, w.c_begin, kDense);
+    ld.load(p, w, kv, cur, kDense, p.ws);
+    ld.store(lds_k[0], lds_v[0]);
+    __syncthreads();
+
+    for (int i = 0; i < n; ++i) {
+      const int stage = i & 1;
+      const bool has_next = i + 1 < n;
+      Step nxt;
+      if (has_next) {
+        nxt = describe_step(w, kv, w.c_begin + i + 1, kDense);
+        ld.load(p, w, kv, nxt, kDense, p.ws);
+      }
+      const S* lk = lds_k[stage];
+      const S* lv = lds_v[stage];
+
+      // S^T[key][row] = K Q^T, two 32-key blocks.
+      f32x16_t s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16_t{};
+#pragma unroll
+        for (int c = 0; c < NQK; ++c) {
+          const auto a = load_frag<E>(lk + (32 * kb + lq) * L::KS + 2 * KPL * c + KPL * hh);
+          s[kb] = mma32(a, qf[c], s[kb]);
+        }
+      }
+
+      const bool full = cur.vlo == 0 && cur.vhi == kChunk;
+      const int last = cur.pos0 + kChunk - 1;
+      const bool clear = full && last <= pmin &&
+                         (kind == SP_GLOBAL || last < sink || cur.pos0 > pmax - window);
+      if (kDense || !clear) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int key = 32 * kb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+            const int j = cur.pos0 + key;
+            bool ok = key >= cur.vlo && key < cur.vhi && j <= p_row;
+            if (kind != SP_GLOBAL) ok = ok && (j < sink || j > p_row - window);
+            s[kb][rr] = ok ? s[kb][rr] : kNegInf;
+          }
+        }
+      }
+
+      // Online softmax in base 2; row statistics are per lane plus the other lane half.
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * p.scale_log2);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = exp2_fast(m_run - m_use);
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const float e = exp2_fast(__builtin_fmaf(s[kb][rr], p.scale_log2, -m_use));
+          s[kb][rr] = e;
+          rs += e;
+        }
+      l_run = l_run * alpha + rs;
+      m_run = m_new;
+      if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+      }
+
+      // O^T[dim][row] += V^T P^T.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int ii = 0; ii < NPV; ++ii) {
+          typename E::Frag b;
+          if constexpr (KPL == 8) {
+            b = to_bf16x8(s[kb][8 * ii + 0], s[kb][8 * ii + 1], s[kb][8 * ii + 2],
+                          s[kb][8 * ii + 3], s[kb][8 * ii + 4], s[kb][8 * ii + 5],
+                          s[kb][8 * ii + 6], s[kb][8 * ii + 7]);
+          } else {
+            b = s[kb][ii];
+          }
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            const auto a =
+                load_frag<E>(lv + (32 * d + lq) * L::VS + 32 * kb + (2 * ii + hh) * KPL);
+            oacc[d] = mma32(a, b, oacc[d]);
+          }
+        }
+      }
+
+      if (has_next) {
+        ld.store(lds_k[stage ^ 1], lds_v[stage ^ 1]);
+        cur = nxt;
+      }
+      __syncthreads();
+    }
+
+    // Epilogue.
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (w.part < 0) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      if (row_ok) {
+        S* dst = obase + orow * D;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int dim = 32 * d + 8 * g4 + 4 * hh;
+            const float o0 = oacc[d][4 * g4 + 0] * inv, o1 = oacc[d][4 * g4 + 1] * inv;
+            const float o2 = oacc[d][4 * g4 + 2] * inv, o3 = oacc[d][4 * g4 + 3] * inv;
+            if constexpr (KPL == 8) {
+              u32x2_t v = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+              *reinterpret_cast<u32x2_t*>(dst + dim) = v;
+            } else {
+              f32x4_t v = {o0, o1, o2, o3};
+              *reinterpret_cast<f32x4_t*>(dst + dim) = v;
+            }
+          }
+        }
+      }
+    } else {
+      float* po = part_o + (int64_t(w.part) * kTileRows + r) * D;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int dim = 32 * d + 8 * g4 + 4 * hh;
+          f32x4_t v = {oacc[d][4 * g4 + 0], oacc[d][4 * g4 + 1], oacc[d][4 * g4 + 2],
+                       oacc[d][4 * g4 + 3]};
+          *reinterpret_cast<f32x4_t*>(po + dim) = v;
+        }
+      }
+      if (hh == 0) {
+        float* pm = part_ml + (int64_t(w.part) * kTileRows + r) * 2;
+        pm[0] = m_run;
+        pm[1] = l_tot;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) retire(p.ws, kOffPrefillCnt, kOffPrefillDone);
+}
+
+// ---------------------------------------------------------------------------------------
+// Decode: persistent, 256 threads, up to 16 rows, split-KV.
+// ---------------------------------------------------------------------------------------
+template <class E, int D, int MODE>
+__global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
+    decode_kernel(AttnParams p) {
+  using S = typename E::S;
+  using L = KVLoader<E, D, false>;
+  constexpr int KPL16 = E::KPL == 8 ? 8 : 1;  // reduction elements per lane, 16x16 QK MFMA
+  constexpr int NQK = D / (4 * KPL16);        // MFMAs for one 16-key block
+  constexpr int ND = D / 16;                  // 16-dim blocks of O^T
+  constexpr bool kDense = MODE == kModeDense;
+  static_assert(2 * L::kKElems * sizeof(S) >= 4 * kDecodeRows * D * sizeof(float),
+                "merge scratch fits the K buffers");
+
+  __shared__ __attribute__((aligned(16))) S lds_k[2][L::kKElems];
+  __shared__ __attribute__((aligned(16))) S lds_v[2][L::kVElems];
+  __shared__ float s_ml[4][kDecodeRows][2];
+  __shared__ int s_item;
+
+  if (!header_ok(p)) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) set_error(p.ws, SP_ERR_PLAN_MISMATCH);
+    return;
+  }
+  const WsHeader* hd = reinterpret_cast<const WsHeader*>(p.ws);
+  const WorkItem* items = reinterpret_cast<const WorkItem*>(p.ws + hd->off_decode);
+  const int32_t* pol = reinterpret_cast<const int32_t*>(p.ws + hd->off_policy);
+  float* part_o = reinterpret_cast<float*>(p.ws + hd->off_part_dec);
+  float* part_ml = reinterpret_cast<float*>(p.ws + hd->off_ml_dec);
+
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int lc = lane & 15, k4 = lane >> 4;
+  const int xcd = blockIdx.x % kXcds;
+  uint32_t exhausted = 0;
+  const S* qbase = static_cast<const S*>(p.q);
+  S* obase = static_cast<S*>(p.o);
+  float* scratch = reinterpret_cast<float*>(&lds_k[0][0]);
+
+  for (;;) {
+    if (tid == 0) s_item = pop_item(p.ws, hd->decode_q, kOffDecodeCnt, xcd, exhausted);
+    __syncthreads();
+    const int it = uniform(s_item);
+    if (it < 0) break;
+    const WorkItem w = load_item(items, it);
+    ItemKV kv;
+    load_item_kv(p, w, kDense, kv, p.ws);
+    const int kind = uniform(pol[w.h * 3 + 0]);
+    const int sink = uniform(pol[w.h * 3 + 1]);
+    const int window = uniform(pol[w.h * 3 + 2]);
+    const int rows = w.nq * p.G;
+
+    // Query row of this lane's MFMA column.
+    const int tl = lc / p.G, g = lc - tl * p.G;
+    const bool row_ok = lc < rows;
+    const int p_row = w.p0 + w.tq0 + tl;
+    const int64_t orow = int64_t(w.q_row0 + w.tq0 + tl) * p.Hq + int64_t(w.h) * p.G + g;
+    typename E::Frag qf[NQK];
+#pragma unroll
+    for (int c = 0; c < NQK; ++c) {
+      qf[c] = row_ok ? load_frag<E>(qbase + orow * D + 4 * KPL16 * c + KPL16 * k4)
+                     : zero_frag<E>();
+    }
+    const int pmin = w.p0 + w.tq0, pmax = pmin + w.nq - 1;
+
+    f32x4_t oacc[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) oacc[d] = f32x4_t{};
+    float m_run = kNegInf, l_run = 0.f;
+
+    L ld;
+    const int n = w.c_end - w.c_begin;
+    Step cur = describe_step(w, kv, w.c_begin, kDense);
+    ld.load(p, w, kv, cur, kDense, p.ws);
+    ld.store(lds_k[0], lds_v[0]);
+    __syncthreads();
+
+    for (int i = 0; i < n; ++i) {
+      const int stage = i & 1;
+      const bool has_next = i + 1 < n;
+      Step nxt;
+      if (has_next) {
+        nxt = describe_step(w, kv, w.c_begin + i + 1, kDense);
+        ld.load(p, w, kv, nxt, kDense, p.ws);
+      }
+      const S* lk = lds_k[stage];
+      const S* lv = lds_v[stage];
+
+      // S^T for keys 16*wave .. 16*wave+15.
+      f32x4_t s = f32x4_t{};
+#pragma unroll
+      for (int c = 0; c < NQK; ++c) {
+        const auto a = load_frag<E>(lk + (16 * wave + lc) * L::KS + 4 * KPL16 * c + KPL16 * k4);
+        s = mma16(a, qf[c], s);
+      }
+      const bool full = cur.vlo == 0 && cur.vhi == kChunk;
+      const int last = cur.pos0 + kChunk - 1;
+      const bool clear = full && last <= pmin &&
+                         (kind == SP_GLOBAL || last < sink || cur.pos0 > pmax - window);
+      if (kDense || !clear) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int key = 16 * wave + 4 * k4 + rr;
+          const int j = cur.pos0 + key;
+          bool ok = key >= cur.vlo && key < cur.vhi && j <= p_row;
+          if (kind != SP_GLOBAL) ok = ok && (j < sink || j > p_row - window);
+          s[rr] = ok ? s[rr] : kNegInf;
+        }
+      }
+      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * p.scale_log2);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = exp2_fast(m_run - m_use);
+      float rs = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float e = exp2_fast(__builtin_fmaf(s[rr], p.scale_log2, -m_use));
+        s[rr] = e;
+        rs += e;
+      }
+      l_run = l_run * alpha + rs;
+      m_run = m_new;
+      if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
+      }
+      // O^T[dim][row] += V^T P^T over this wave's 16 keys.
+      if constexpr (E::KPL == 8) {
+        const s16x4_t b = __builtin_bit_cast(
+            s16x4_t, u32x2_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])});
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const s16x4_t a = *reinterpret_cast<const s16x4_t*>(lv + (16 * d + lc) * L::VS +
+                                                              16 * wave + 4 * k4);
+          oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, oacc[d], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            const float a = lv[(16 * d + lc) * L::VS + 16 * wave + 4 * k4 + rr];
+            oacc[d] = mma16(a, s[rr], oacc[d]);
+          }
+        }
+      }
+
+      if (has_next) {
+        ld.store(lds_k[stage ^ 1], lds_v[stage ^ 1]);
+        cur = nxt;
+      }
+      __syncthreads();
+    }
+
+    // Merge the four waves' partial softmax states through LDS.
+    float l_w = l_run + __shfl_xor(l_run, 16);
+    l_w += __shfl_xor(l_w, 32);
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        scratch[(wave * kDecodeRows + lc) * D + 16 * d + 4 * k4 + rr] = oacc[d][rr];
+    if (k4 == 0) {
+      s_ml[wave][lc][0] = m_run;
+      s_ml[wave][lc][1] = l_w;
+    }
+    __syncthreads();
+    for (int e = tid; e < kDecodeRows * D; e += 256) {
+      const int q = e / D, dim = e - q * D;
+      if (q >= rows) continue;
+      float M = kNegInf;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_ml[ww][q][0]);
+      const float Mu = M == kNegInf ? 0.f : M;
+      float acc = 0.f, lsum = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float f = exp2_fast(s_ml[ww][q][0] - Mu);
+        acc += f * scratch[(ww * kDecodeRows + q) * D + dim];
+        lsum += f * s_ml[ww][q][1];
+      }
+      const int tq = q / p.G, gq = q - tq * p.G;
+      if (w.part < 0) {
+        const int64_t orw = int64_t(w.q_row0 + w.tq0 + tq) * p.Hq + int64_t(w.h) * p.G + gq;
+        const float val = lsum > 0.f ? acc / lsum : 0.f;
+        if constexpr (E::KPL == 8) {
+          obase[orw * D + dim] = uint16_t(pack_bf16x2(val, 0.f) & 0xffffu);
+        } else {
+          obase[orw * D + dim] = val;
+        }
+      } else {
+        part_o[(int64_t(w.part) * kDecodeRows + q) * D + dim] = acc;
+        if (dim == 0) {
+          part_ml[(int64_t(w.part) * kDecodeRows + q) * 2 + 0] = M;
+          part_ml[(int64_t(w.part) * kDecodeRows + q) * 2 + 1] = lsum;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) retire(p.ws, kOffDecodeCnt, kOffDecodeDone);
+}
+
+// ---------------------------------------------------------------------------------------
+// Combine: merges the partials of each KV-split block in split order.
+// ---------------------------------------------------------------------------------------
+template <class E, int D>
+__global__ void __launch_bounds__(256) combine_kernel(AttnParams p) {
+  using S = typename E::S;
+  if (!header_ok(p)) return;
+  const WsHeader* hd = reinterpret_cast<const WsHeader*>(p.ws);
+  const CombineItem* items = reinterpret_cast<const CombineItem*>(p.ws + hd->off_combine);
+  S* obase = static_cast<S*>(p.o);
+  for (int ci = blockIdx.x; ci < hd->n_combine; ci += gridDim.x) {
+    const CombineItem c = items[ci];
+    const int rows_max = c.kind == 0 ? kTileRows : kDecodeRows;
+    const float* po = reinterpret_cast<const float*>(p.ws + (c.kind == 0 ? hd->off_part_pre
+                                                                        : hd->off_part_dec));
+    const float* pm = reinterpret_cast<const float*>(p.ws + (c.kind == 0 ? hd->off_ml_pre
+                                                                        : hd->off_ml_dec));
+    const int rows = c.nq * p.G;
+    for (int e = threadIdx.x; e < rows * (D / 4); e += blockDim.x) {
+      const int r = e / (D / 4), d4 = e - r * (D / 4);
+      float M = kNegInf;
+      for (int s = 0; s < c.nsplit; ++s)
+        M = fmaxf(M, pm[(int64_t(c.part0 + s) * rows_max + r) * 2]);
+      const float Mu = M == kNegInf ? 0.f : M;
+      f32x4_t acc = f32x4_t{};
+      float lsum = 0.f;
+      for (int s = 0; s < c.nsplit; ++s) {
+        const int64_t slot = int64_t(c.part0 + s) * rows_max + r;
+        const float f = exp2_fast(pm[slot * 2] - Mu);
+        lsum += f * pm[slot * 2 + 1];
+        acc += f * *reinterpret_cast<const f32x4_t*>(po + slot * D + 4 * d4);
+      }
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      acc *= inv;
+      const int tq = r / p.G, g = r - tq * p.G;
+      const int64_t orow = int64_t(c.q_row0 + c.tq0 + tq) * p.Hq + int64_t(c.h) * p.G + g;
+      if constexpr (sizeof(S) == 2) {
+        u32x2_t v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+        *reinterpret_cast<u32x2_t*>(obase + orow * D + 4 * d4) = v;
+      } else {
+        *reinterpret_cast<f32x4_t*>(obase + orow * D + 4 * d4) = acc;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Build / scatter: one work group copies 64 stored tokens (K and V) of one segment from the
+// dense [T][Hkv][D] tensors into their pool pages. Reads are whole D-rows, writes are whole
+// contiguous page rows.
+// ---------------------------------------------------------------------------------------
+template <class E, int D>
+__global__ void __launch_bounds__(256) build_kernel(BuildParams p) {
+  using S = typename E::S;
+  constexpr int kVec = E::kVec;
+  constexpr int kCols = D / kVec;
+  constexpr int kLoads = kChunk * kCols / 256;
+  const int c = blockIdx.x;
+  // Segment of this unit: last entry with chunk0 <= c (kernel arguments, uniform).
+  int lo = 0, hi = p.nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.seg[mid].chunk0 <= c) lo = mid; else hi = mid - 1;
+  }
+  const BuildSeg sg = p.seg[lo];
+  const int ti0 = (c - sg.chunk0) * kChunk;
+  const S* kd = static_cast<const S*>(p.k);
+  const S* vd = static_cast<const S*>(p.v);
+  S* kp = static_cast<S*>(p.kp);
+  S* vp = static_cast<S*>(p.vp);
+  u32x4_t kr[kLoads], vr[kLoads];
+  int64_t dst[kLoads];
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int idx = threadIdx.x + 256 * j;
+    const int row = idx / kCols, col = idx % kCols;
+    const int ti = ti0 + row;
+    dst[j] = -1;
+    kr[j] = vr[j] = u32x4_t{0u, 0u, 0u, 0u};
+    if (ti < sg.ntok) {
+      const int64_t src = (int64_t(sg.src_row0 + ti) * p.Hkv + sg.h) * D + col * kVec;
+      kr[j] = *reinterpret_cast<const u32x4_t*>(kd + src);
+      vr[j] = *reinterpret_cast<const u32x4_t*>(vd + src);
+      const int phys = p.v2p[sg.vstart + ti / p.P];
+      dst[j] = (int64_t(phys) * p.P + (ti & (p.P - 1))) * D + col * kVec;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    if (dst[j] >= 0) {
+      *reinterpret_cast<u32x4_t*>(kp + dst[j]) = kr[j];
+      *reinterpret_cast<u32x4_t*>(vp + dst[j]) = vr[j];
+    }
+  }
+}
+
+template <class E, int D, int MODE>
+int occ_of(bool decode) {
+  int n = 0;
+  hipError_t e;
+  if (decode)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<E, D, MODE>, 256, 0);
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_kernel<E, D, MODE>, 256, 0);
+  if (e != hipSuccess || n < 1) n = 1;
+  return n;
+}
+
+template <class E, int D, int MODE>
+hipError_t launch_attn_t(bool decode, int grid, const AttnParams& p, hipStream_t st) {
+  if (decode)
+    decode_kernel<E, D, MODE><<<grid, 256, 0, st>>>(p);
+  else
+    prefill_kernel<E, D, MODE><<<grid, 256, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+#define SP_DISPATCH(DTYPE, DIM, MODE, CALL)                                  \
+  do {                                                                       \
+    if ((DTYPE) == SP_BF16) {                                                \
+      if ((DIM) == 64) {                                                     \
+        if ((MODE) == kModePaged) { CALL(BF16, 64, kModePaged); }            \
+        else { CALL(BF16, 64, kModeDense); }                                 \
+      } else {                                                               \
+        if ((MODE) == kModePaged) { CALL(BF16, 128, kModePaged); }           \
+        else { CALL(BF16, 128, kModeDense); }                                \
+      }                                                                      \
+    } else {                                                                 \
+      if ((DIM) == 64) {                                                     \
+        if ((MODE) == kModePaged) { CALL(F32, 64, kModePaged); }             \
+        else { CALL(F32, 64, kModeDense); }                                  \
+      } else {                                                               \
+        if ((MODE) == kModePaged) { CALL(F32, 128, kModePaged); }            \
+        else { CALL(F32, 128, kModeDense); }                                 \
+      }                                                                      \
+    }                                                                        \
+  } while (0)
+
+int attention_occupancy(int32_t dtype, int32_t D, int32_t mode, bool decode) {
+  int n = 1;
+#define SP_OCC(E, DD, M) n = occ_of<E, DD, M>(decode)
+  SP_DISPATCH(dtype, D, mode, SP_OCC);
+#undef SP_OCC
+  return n;
+}
+
+hipError_t launch_attention(int32_t dtype, int32_t D, int32_t mode, bool decode, int grid,
+                            const AttnParams& p, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+#define SP_LAUNCH(E, DD, M) e = launch_attn_t<E, DD, M>(decode, grid, p, stream)
+  SP_DISPATCH(dtype, D, mode, SP_LAUNCH);
+#undef SP_LAUNCH
+  return e;
+}
+
+hipError_t launch_combine(int32_t dtype, int32_t D, int grid, const AttnParams& p,
+                          hipStream_t stream) {
+  if (dtype == SP_BF16) {
+    if (D == 64) combine_kernel<BF16, 64><<<grid, 256, 0, stream>>>(p);
+    else combine_kernel<BF16, 128><<<grid, 256, 0, stream>>>(p);
+  } else {
+    if (D == 64) combine_kernel<F32, 64><<<grid, 256, 0, stream>>>(p);
+    else combine_kernel<F32, 128><<<grid, 256, 0, stream>>>(p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_build(int32_t dtype, int32_t D, const BuildParams& p, hipStream_t stream) {
+  if (p.nchunks <= 0) return hipSuccess;
+  if (dtype == SP_BF16) {
+    if (D == 64) build_kernel<BF16, 64><<<p.nchunks, 256, 0, stream>>>(p);
+    else build_kernel<BF16, 128><<<p.nchunks, 256, 0, stream>>>(p);
+  } else {
+    if (D == 64) build_kernel<F32, 64><<<p.nchunks, 256, 0, stream>>>(p);
+    else build_kernel<F32, 128><<<p.nchunks, 256, 0, stream>>>(p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sp

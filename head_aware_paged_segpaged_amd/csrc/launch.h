@@ -1,0 +1,55 @@
+// Kernel parameter blocks and launchers of libsegpaged (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sp_common.h"
+
+namespace sp {
+
+struct AttnParams {
+  const void* q;
+  void* o;
+  const void* k;  // K pool [n_phys][P][D] (paged) or dense K [T][Hkv][D]
+  const void* v;
+  const int32_t* seg_table;  // paged only
+  const int32_t* kv_len;     // paged only
+  const int32_t* v2p;        // paged only
+  int64_t n_phys;
+  uint8_t* ws;
+  uint64_t signature;
+  uint64_t ws_bytes;
+  int32_t Hq, Hkv, G, P;
+  float scale_log2;  // softmax_scale * log2(e)
+};
+
+struct BuildSeg {
+  int32_t chunk0;    // first 64-token copy unit of this segment in the launch
+  int32_t src_row0;  // dense row of the segment's first stored token
+  int32_t vstart;    // first virtual page of the segment
+  int32_t ntok;
+  int32_t h;
+};
+
+constexpr int kMaxBuildSegs = 128;
+
+struct BuildParams {
+  const void* k;
+  const void* v;
+  void* kp;
+  void* vp;
+  const int32_t* v2p;
+  int32_t Hkv, P, nseg, nchunks;
+  BuildSeg seg[kMaxBuildSegs];
+};
+
+// Resident work groups per compute unit of the persistent attention kernels.
+int attention_occupancy(int32_t dtype, int32_t D, int32_t mode, bool decode);
+hipError_t launch_attention(int32_t dtype, int32_t D, int32_t mode, bool decode, int grid,
+                            const AttnParams& p, hipStream_t stream);
+hipError_t launch_combine(int32_t dtype, int32_t D, int grid, const AttnParams& p,
+                          hipStream_t stream);
+hipError_t launch_build(int32_t dtype, int32_t D, const BuildParams& p, hipStream_t stream);
+
+}  // namespace sp

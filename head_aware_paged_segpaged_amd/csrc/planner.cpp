@@ -1,0 +1,407 @@
+// Host planning: validation, per-head page layout, attention work list.
+//
+// Layout rules (page "RedKnot SegPagedAttention runtime design", section 3): every (layer,
+// head, segment) owns contiguous virtual pages; GLOBAL heads keep the whole context, LOCAL
+// heads only the sink and the recent tokens any query of the chunk can see. The work list
+// realises section 4 of the same page: every (query head, KV head) pair in one launch, each
+// head walking only its own stored tokens.
+#include "planner.h"
+
+#include <algorithm>
+#include <cstring>
+#include <numeric>
+
+namespace sp {
+
+namespace {
+
+constexpr int64_t kInt32Max = 0x7fffffffLL;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Number of 64-aligned KV steps covering [begin, end) of a segment.
+int32_t range_steps(const Range& r) {
+  if (r.end <= r.begin) return 0;
+  return int32_t(ceil_div(r.end, kChunk) - r.begin / kChunk);
+}
+
+uint64_t fnv(uint64_t h, uint64_t v) {
+  for (int i = 0; i < 8; ++i) {
+    h ^= (v >> (8 * i)) & 0xff;
+    h *= 0x100000001b3ull;
+  }
+  return h;
+}
+
+}  // namespace
+
+sp_status check_dtype_dim(int32_t dtype, int32_t D) {
+  if (dtype != SP_BF16 && dtype != SP_F32) return SP_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return SP_ERR_UNSUPPORTED;
+  return SP_OK;
+}
+
+sp_status check_page_size(int32_t P) {
+  if (P != 16 && P != 32 && P != 64 && P != 128 && P != 256) return SP_ERR_UNSUPPORTED;
+  return SP_OK;
+}
+
+sp_status check_lengths_policy(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                               int32_t Hkv, const sp_head_policy* pol) {
+  if (B < 0 || Hkv < 1) return SP_ERR_INVALID_ARG;
+  if (B > 0 && (ctx_len == nullptr || q_len == nullptr)) return SP_ERR_INVALID_ARG;
+  if (pol == nullptr) return SP_ERR_INVALID_ARG;
+  for (int32_t h = 0; h < Hkv; ++h) {
+    if (pol[h].kind == SP_GLOBAL) continue;
+    if (pol[h].kind != SP_LOCAL) return SP_ERR_INVALID_ARG;
+    if (pol[h].sink < 0 || pol[h].window < 1) return SP_ERR_INVALID_ARG;
+  }
+  int64_t tot_ctx = 0, tot_q = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (ctx_len[b] < 0 || q_len[b] < 0 || q_len[b] > ctx_len[b]) return SP_ERR_INVALID_ARG;
+    tot_ctx += ctx_len[b];
+    tot_q += q_len[b];
+  }
+  if (tot_ctx > kInt32Max || tot_q > kInt32Max) return SP_ERR_UNSUPPORTED;
+  return SP_OK;
+}
+
+sp_status check_shape(const Shape& s) {
+  sp_status st = check_dtype_dim(s.dtype, s.D);
+  if (st != SP_OK) return st;
+  if (s.mode == kModePaged) {
+    st = check_page_size(s.P);
+    if (st != SP_OK) return st;
+  }
+  if (s.Hkv < 1 || s.Hq < 1 || s.Hq % s.Hkv != 0) return SP_ERR_INVALID_ARG;
+  if (s.Hq / s.Hkv > kTileRows) return SP_ERR_UNSUPPORTED;
+  st = check_lengths_policy(s.B, s.ctx_len, s.q_len, s.Hkv, s.pol);
+  if (st != SP_OK) return st;
+  int64_t tot_q = 0;
+  for (int32_t b = 0; b < s.B; ++b) tot_q += s.q_len[b];
+  if (tot_q * s.Hq > kInt32Max) return SP_ERR_UNSUPPORTED;  // int32 O/Q row ids in kernels
+  return SP_OK;
+}
+
+int head_segments(const sp_head_policy& pol, int32_t L, int32_t q, int32_t out_pos[2],
+                  int32_t out_ntok[2]) {
+  if (L <= 0) return 0;
+  if (pol.kind == SP_GLOBAL) {
+    out_pos[0] = 0;
+    out_ntok[0] = L;
+    return 1;
+  }
+  const int64_t s = std::min<int64_t>(pol.sink, L);
+  const int64_t r0 = std::max<int64_t>(0, int64_t(L) - q - pol.window + 1);
+  if (r0 <= s) {
+    out_pos[0] = 0;
+    out_ntok[0] = L;
+    return 1;
+  }
+  if (s == 0) {
+    out_pos[0] = int32_t(r0);
+    out_ntok[0] = int32_t(L - r0);
+    return 1;
+  }
+  out_pos[0] = 0;
+  out_ntok[0] = int32_t(s);
+  out_pos[1] = int32_t(r0);
+  out_ntok[1] = int32_t(L - r0);
+  return 2;
+}
+
+sp_status make_layout(int32_t B, const int32_t* ctx_len, const int32_t* q_len, int32_t Hkv,
+                      const sp_head_policy* pol, int32_t P, Layout* out) {
+  out->heads.assign(size_t(B) * Hkv, HeadLayout{});
+  int64_t v = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    for (int32_t h = 0; h < Hkv; ++h) {
+      HeadLayout& hl = out->heads[size_t(b) * Hkv + h];
+      int32_t pos[2] = {0, 0}, ntok[2] = {0, 0};
+      hl.nseg = head_segments(pol[h], ctx_len[b], q_len[b], pos, ntok);
+      hl.kv_len = 0;
+      for (int s = 0; s < 2; ++s) {
+        Segment& sg = hl.seg[s];
+        if (s < hl.nseg) {
+          sg.pos = pos[s];
+          sg.ntok = ntok[s];
+          sg.vstart = int32_t(v);
+          sg.npages = int32_t(ceil_div(ntok[s], P));
+          v += sg.npages;
+          hl.kv_len += ntok[s];
+        } else {
+          sg = Segment{0, 0, int32_t(v), 0};
+        }
+        if (v > kInt32Max) return SP_ERR_UNSUPPORTED;
+      }
+    }
+  }
+  out->n_virt = v;
+  return SP_OK;
+}
+
+void layout_tables(const Layout& lay, int32_t B, int32_t Hkv, int32_t* seg_table,
+                   int32_t* kv_len) {
+  for (int32_t i = 0; i < B * Hkv; ++i) {
+    const HeadLayout& hl = lay.heads[i];
+    for (int s = 0; s < 2; ++s) {
+      int32_t* e = seg_table + (size_t(i) * 2 + s) * 4;
+      e[0] = hl.seg[s].pos;
+      e[1] = hl.seg[s].ntok;
+      e[2] = hl.seg[s].vstart;
+      e[3] = hl.seg[s].npages;
+    }
+    kv_len[i] = hl.kv_len;
+  }
+}
+
+uint64_t shape_signature(const Shape& s, int32_t slots_prefill, int32_t slots_decode) {
+  uint64_t h = 0xcbf29ce484222325ull;
+  const int64_t fields[] = {s.mode, s.dtype, s.B, s.Hq, s.Hkv, s.D,
+                            s.mode == kModePaged ? s.P : 0, slots_prefill, slots_decode};
+  for (int64_t f : fields) h = fnv(h, uint64_t(f));
+  for (int32_t b = 0; b < s.B; ++b) h = fnv(h, (uint64_t(uint32_t(s.ctx_len[b])) << 32) |
+                                                   uint32_t(s.q_len[b]));
+  for (int32_t i = 0; i < s.Hkv; ++i) {
+    h = fnv(h, uint64_t(uint32_t(s.pol[i].kind)));
+    if (s.pol[i].kind == SP_LOCAL)
+      h = fnv(h, (uint64_t(uint32_t(s.pol[i].sink)) << 32) | uint32_t(s.pol[i].window));
+  }
+  return h;
+}
+
+void needed_kernels(const Shape& s, bool* prefill, bool* decode) {
+  const int32_t G = s.Hq / s.Hkv;
+  *prefill = *decode = false;
+  for (int32_t b = 0; b < s.B; ++b) {
+    if (s.q_len[b] == 0) continue;
+    if (int64_t(s.q_len[b]) * G <= kDecodeRows)
+      *decode = true;
+    else
+      *prefill = true;
+  }
+}
+
+namespace {
+
+// The KV ranges a block of queries at positions [pmin, pmax] of one head must read.
+void tile_ranges(const Shape& s, const HeadLayout* hl, const sp_head_policy& pol, int32_t pmin,
+                 int32_t pmax, int32_t L, Range* ra, Range* rb) {
+  *ra = Range{0, 0, 0};
+  *rb = Range{0, 0, 0};
+  if (s.mode == kModeDense || pol.kind == SP_GLOBAL) {
+    *ra = Range{0, 0, pmax + 1};
+    return;
+  }
+  const int32_t sink = std::min(pol.sink, L);
+  const int32_t lo = int32_t(std::max<int64_t>(0, int64_t(pmin) - pol.window + 1));
+  if (hl->nseg == 1 && hl->seg[0].pos == 0) {  // one merged segment (0, L)
+    if (lo <= sink) {
+      *ra = Range{0, 0, pmax + 1};
+    } else {
+      if (sink > 0) *ra = Range{0, 0, sink};
+      *rb = Range{0, lo, pmax + 1};
+    }
+  } else if (hl->nseg == 1) {  // recent part only (sink 0)
+    const int32_t r0 = hl->seg[0].pos;
+    *ra = Range{0, lo - r0, pmax + 1 - r0};
+  } else {  // sink segment + recent segment
+    const int32_t r0 = hl->seg[1].pos;
+    *ra = Range{0, 0, sink};
+    *rb = Range{1, lo - r0, pmax + 1 - r0};
+  }
+  if (ra->end <= ra->begin) {
+    *ra = *rb;
+    *rb = Range{0, 0, 0};
+  }
+}
+
+struct Tile {
+  WorkItem w;
+  int32_t steps;
+  int32_t split;  // index of this split within its tile
+};
+
+// Splits long tiles along KV so that no item is much longer than the average load of one
+// work-group slot, then returns the items and the combine list.
+void split_tiles(std::vector<Tile>& tiles, int32_t slots, int32_t min_split, int32_t kind,
+                 std::vector<Tile>* items, std::vector<CombineItem>* combine, int32_t* n_part) {
+  int64_t total = 0;
+  for (const Tile& t : tiles) total += t.steps + kItemOverhead;
+  const int64_t avg = slots > 0 ? ceil_div(total, slots) : total;
+  const int32_t target = int32_t(std::max<int64_t>(min_split, avg));
+  for (const Tile& t : tiles) {
+    const int32_t ns = int32_t(std::max<int64_t>(1, ceil_div(t.steps, target)));
+    if (ns == 1) {
+      Tile x = t;
+      x.w.part = -1;
+      items->push_back(x);
+      continue;
+    }
+    const int32_t part0 = *n_part;
+    *n_part += ns;
+    for (int32_t k = 0; k < ns; ++k) {
+      Tile x = t;
+      const int32_t c0 = int32_t(int64_t(t.steps) * k / ns);
+      const int32_t c1 = int32_t(int64_t(t.steps) * (k + 1) / ns);
+      x.w.c_begin = c0;
+      x.w.c_end = c1;
+      x.w.part = part0 + k;
+      x.steps = c1 - c0;
+      x.split = k;
+      items->push_back(x);
+    }
+    combine->push_back(CombineItem{t.w.b, t.w.h, t.w.tq0, t.w.nq, part0, ns, t.w.q_row0, kind});
+  }
+}
+
+// Cuts the locality-ordered items into kXcds contiguous runs of about equal cost (one queue
+// per XCD, so tiles that read the same KV share an L2), then orders each queue longest first.
+void make_queues(std::vector<Tile>& items, std::vector<WorkItem>* out, int32_t* bounds) {
+  std::stable_sort(items.begin(), items.end(), [](const Tile& a, const Tile& b) {
+    if (a.w.b != b.w.b) return a.w.b < b.w.b;
+    if (a.w.h != b.w.h) return a.w.h < b.w.h;
+    if (a.split != b.split) return a.split < b.split;
+    return a.w.tq0 < b.w.tq0;
+  });
+  int64_t total = 0;
+  for (const Tile& t : items) total += t.steps + kItemOverhead;
+  std::vector<int32_t> cut(kXcds + 1, int32_t(items.size()));
+  cut[0] = 0;
+  int64_t acc = 0;
+  int x = 1;
+  for (size_t i = 0; i < items.size() && x < kXcds; ++i) {
+    acc += items[i].steps + kItemOverhead;
+    while (x < kXcds && acc * kXcds >= total * x) cut[x++] = int32_t(i + 1);
+  }
+  out->clear();
+  for (int q = 0; q < kXcds; ++q) {
+    std::stable_sort(items.begin() + cut[q], items.begin() + cut[q + 1],
+                     [](const Tile& a, const Tile& b) { return a.steps > b.steps; });
+    bounds[q] = int32_t(out->size());
+    for (int32_t i = cut[q]; i < cut[q + 1]; ++i) out->push_back(items[i].w);
+  }
+  bounds[kXcds] = int32_t(out->size());
+}
+
+}  // namespace
+
+sp_status make_plan(const Shape& s, int32_t slots_prefill, int32_t slots_decode, Plan* out) {
+  Layout lay;
+  if (s.mode == kModePaged) {
+    sp_status st = make_layout(s.B, s.ctx_len, s.q_len, s.Hkv, s.pol, s.P, &lay);
+    if (st != SP_OK) return st;
+  }
+  const int32_t G = s.Hq / s.Hkv;
+  std::vector<Tile> pre_tiles, dec_tiles;
+  int32_t q_row0 = 0, kv_row0 = 0;
+  for (int32_t b = 0; b < s.B; ++b) {
+    const int32_t L = s.ctx_len[b], nq = s.q_len[b];
+    if (nq > 0) {
+      const bool dec = int64_t(nq) * G <= kDecodeRows;
+      const int32_t bq = dec ? nq : std::max(1, kTileRows / G);
+      const int32_t p0 = L - nq;
+      for (int32_t h = 0; h < s.Hkv; ++h) {
+        const HeadLayout* hl =
+            s.mode == kModePaged ? &lay.heads[size_t(b) * s.Hkv + h] : nullptr;
+        for (int32_t t0 = 0; t0 < nq; t0 += bq) {
+          const int32_t nt = std::min(bq, nq - t0);
+          const int32_t pmin = p0 + t0, pmax = pmin + nt - 1;
+          Range ra, rb;
+          tile_ranges(s, hl, s.pol[h], pmin, pmax, L, &ra, &rb);
+          Tile t{};
+          WorkItem& w = t.w;
+          w.b = b;
+          w.h = h;
+          w.tq0 = t0;
+          w.nq = nt;
+          w.ra_seg = ra.seg;
+          w.ra_begin = ra.begin;
+          w.ra_end = ra.end;
+          w.rb_seg = rb.seg;
+          w.rb_begin = rb.begin;
+          w.rb_end = rb.end;
+          t.steps = range_steps(ra) + range_steps(rb);
+          w.c_begin = 0;
+          w.c_end = t.steps;
+          w.part = -1;
+          w.q_row0 = q_row0;
+          w.p0 = p0;
+          w.kv_row0 = kv_row0;
+          t.split = 0;
+          (dec ? dec_tiles : pre_tiles).push_back(t);
+        }
+      }
+    }
+    q_row0 += nq;
+    kv_row0 += L;
+  }
+
+  std::vector<Tile> pre_items, dec_items;
+  std::vector<CombineItem> combine;
+  int32_t n_part_pre = 0, n_part_dec = 0;
+  split_tiles(pre_tiles, slots_prefill, /*min_split=*/16, 0, &pre_items, &combine, &n_part_pre);
+  split_tiles(dec_tiles, slots_decode, /*min_split=*/32, 1, &dec_items, &combine, &n_part_dec);
+
+  WsHeader& hd = out->hdr;
+  std::memset(&hd, 0, sizeof(hd));
+  make_queues(pre_items, &out->prefill, hd.prefill_q);
+  make_queues(dec_items, &out->decode, hd.decode_q);
+  out->combine = combine;
+  out->policy.resize(size_t(s.Hkv) * 3);
+  for (int32_t h = 0; h < s.Hkv; ++h) {
+    out->policy[h * 3 + 0] = s.pol[h].kind;
+    out->policy[h * 3 + 1] = s.pol[h].kind == SP_LOCAL ? s.pol[h].sink : 0;
+    out->policy[h * 3 + 2] = s.pol[h].kind == SP_LOCAL ? s.pol[h].window : 1;
+  }
+
+  hd.magic = kMagic;
+  hd.signature = shape_signature(s, slots_prefill, slots_decode);
+  hd.n_prefill = int32_t(out->prefill.size());
+  hd.n_decode = int32_t(out->decode.size());
+  hd.n_combine = int32_t(out->combine.size());
+  hd.n_part_pre = n_part_pre;
+  hd.n_part_dec = n_part_dec;
+  size_t off = kHeaderBytes;
+  hd.off_prefill = int64_t(off);
+  off = align256(off + out->prefill.size() * sizeof(WorkItem));
+  hd.off_decode = int64_t(off);
+  off = align256(off + out->decode.size() * sizeof(WorkItem));
+  hd.off_combine = int64_t(off);
+  off = align256(off + out->combine.size() * sizeof(CombineItem));
+  hd.off_policy = int64_t(off);
+  off = align256(off + out->policy.size() * sizeof(int32_t));
+  out->upload_bytes = off;
+  const size_t fbytes = 4;
+  hd.off_part_pre = int64_t(off);
+  off = align256(off + size_t(n_part_pre) * kTileRows * s.D * fbytes);
+  hd.off_ml_pre = int64_t(off);
+  off = align256(off + size_t(n_part_pre) * kTileRows * 2 * fbytes);
+  hd.off_part_dec = int64_t(off);
+  off = align256(off + size_t(n_part_dec) * kDecodeRows * s.D * fbytes);
+  hd.off_ml_dec = int64_t(off);
+  off = align256(off + size_t(n_part_dec) * kDecodeRows * 2 * fbytes);
+  out->bytes = off;
+  hd.bytes = off;
+  return SP_OK;
+}
+
+void serialize_plan(const Plan& plan, std::vector<uint8_t>* buf) {
+  buf->assign(plan.upload_bytes, 0);
+  uint8_t* p = buf->data();
+  std::memcpy(p, &plan.hdr, sizeof(WsHeader));
+  if (!plan.prefill.empty())
+    std::memcpy(p + plan.hdr.off_prefill, plan.prefill.data(),
+                plan.prefill.size() * sizeof(WorkItem));
+  if (!plan.decode.empty())
+    std::memcpy(p + plan.hdr.off_decode, plan.decode.data(),
+                plan.decode.size() * sizeof(WorkItem));
+  if (!plan.combine.empty())
+    std::memcpy(p + plan.hdr.off_combine, plan.combine.data(),
+                plan.combine.size() * sizeof(CombineItem));
+  std::memcpy(p + plan.hdr.off_policy, plan.policy.data(), plan.policy.size() * sizeof(int32_t));
+}
+
+}  // namespace sp

@@ -1,0 +1,78 @@
+// Host-side planning for libsegpaged: argument validation, the per-head page layout and the
+// attention work list. Pure integer C++; no HIP calls.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "segpaged.h"
+#include "sp_common.h"
+
+namespace sp {
+
+struct Segment {
+  int32_t pos, ntok, vstart, npages;
+};
+
+struct HeadLayout {
+  Segment seg[2];
+  int32_t nseg;
+  int32_t kv_len;
+};
+
+// Page layout of one batch: heads[b * Hkv + h].
+struct Layout {
+  std::vector<HeadLayout> heads;
+  int64_t n_virt = 0;
+};
+
+// Shape arguments common to the attention calls.
+struct Shape {
+  int32_t mode;  // kModePaged or kModeDense
+  int32_t dtype;
+  int32_t B, Hq, Hkv, D, P;
+  const int32_t* ctx_len;
+  const int32_t* q_len;
+  const sp_head_policy* pol;
+};
+
+sp_status check_dtype_dim(int32_t dtype, int32_t D);
+sp_status check_page_size(int32_t P);
+sp_status check_lengths_policy(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                               int32_t Hkv, const sp_head_policy* pol);
+sp_status check_shape(const Shape& s);
+
+// Segments of one (request, KV head) following the layout rules of include/segpaged.h.
+int head_segments(const sp_head_policy& pol, int32_t L, int32_t q, int32_t out_pos[2],
+                  int32_t out_ntok[2]);
+
+sp_status make_layout(int32_t B, const int32_t* ctx_len, const int32_t* q_len, int32_t Hkv,
+                      const sp_head_policy* pol, int32_t P, Layout* out);
+
+// Fills seg_table [B][Hkv][2][4] and kv_len [B][Hkv] from a layout.
+void layout_tables(const Layout& lay, int32_t B, int32_t Hkv, int32_t* seg_table,
+                   int32_t* kv_len);
+
+uint64_t shape_signature(const Shape& s, int32_t slots_prefill, int32_t slots_decode);
+
+struct Plan {
+  WsHeader hdr;
+  std::vector<WorkItem> prefill, decode;
+  std::vector<CombineItem> combine;
+  std::vector<int32_t> policy;  // [Hkv][3]
+  size_t bytes = 0;             // whole workspace
+  size_t upload_bytes = 0;      // header + item arrays + policy (what the plan call copies)
+};
+
+sp_status make_plan(const Shape& s, int32_t slots_prefill, int32_t slots_decode, Plan* out);
+
+// Header, counters (zero), item arrays and policy table as one host buffer of
+// plan.upload_bytes bytes, laid out exactly as in the workspace.
+void serialize_plan(const Plan& plan, std::vector<uint8_t>* buf);
+
+// Which kernels a call needs (cheap, from the host arrays only).
+void needed_kernels(const Shape& s, bool* prefill, bool* decode);
+
+}  // namespace sp

@@ -1,0 +1,209 @@
+/*
+ * segpaged.h -- C ABI of libsegpaged.so: head-aware SegPaged attention on AMD CDNA4 (gfx950).
+ *
+ * Method (page "RedKnot SegPagedAttention runtime design", sections 1-4): every KV head owns
+ * its own page table over one shared physical page pool. A GLOBAL head stores and reads the
+ * whole context. A LOCAL head stores and reads only its first S "sink" tokens plus a recent
+ * window of W tokens. Attention then packs every (query head, KV head) pair into one
+ * variable-length launch in which each head walks only its own stored pages, so LOCAL heads
+ * neither hold nor move KV they cannot see.
+ *
+ * Calls, in the order a caller makes them:
+ *   segpaged_plan_pages           host only: how many pages a layout needs
+ *   segpaged_layout_tables        host only: the tables segpaged_build will write
+ *   segpaged_build                once per layout: page tables + fill the pool from dense K/V
+ *   segpaged_attention_workspace_size / segpaged_attention_plan
+ *                                 once per layout: the work list the attention kernels pop
+ *   segpaged_attention            every call: O = attention(Q, paged K/V)
+ * The dense-plus-mask comparison path (segpaged_dense_mask_*) reads dense K/V directly.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - B requests; request b has ctx_len[b] context tokens and a query chunk of q_len[b] tokens,
+ *   the LAST q_len[b] positions of its context: query token t sits at absolute position
+ *   p = ctx_len[b] - q_len[b] + t. 0 <= q_len[b] <= ctx_len[b].
+ * - Hq query heads over Hkv KV heads, G = Hq / Hkv an integer; query head hq reads KV head
+ *   hq / G (contiguous groups).
+ * - Visibility of key position j to a query at position p:
+ *     GLOBAL: j <= p;   LOCAL: j <= p and (j < sink or j > p - window).
+ * - Dense K/V are token-major with requests concatenated: [sum(ctx_len), Hkv, D], request b's
+ *   rows start at sum_{b'<b} ctx_len[b']. Q and O are [sum(q_len), Hq, D]. Rows are dense
+ *   (row stride Hkv*D or Hq*D elements).
+ * - Element type: SP_BF16 (bfloat16 storage, fp32 accumulation and softmax, probabilities
+ *   rounded to bf16 before P*V, O rounded to nearest even) or SP_F32 (fp32 throughout).
+ * - Supported: D in {64, 128}; page_size in {16, 32, 64, 128, 256}; 1 <= G <= 128;
+ *   sink >= 0; window >= 1.
+ * - Pointers named "host" are read before the call returns. Pointers named "device" are
+ *   device memory owned by the caller; the library allocates no device memory and keeps no
+ *   state between calls. Device work is queued on `stream` and is asynchronous unless a call
+ *   says otherwise.
+ * - Errors: every argument is validated on the host before anything is queued; a call that
+ *   returns an error has written nothing. The library never aborts and never throws.
+ *
+ * Page layout written by segpaged_build (page "RedKnot SegPagedAttention runtime design",
+ * section 3: (layer, head, segment) -> contiguous virtual pages; a virtual -> physical map
+ * over a shared pool; LOCAL heads keep only sink + recent tokens):
+ * - A LOCAL head's recent part starts at R0 = max(0, L - q - W + 1), the earliest position
+ *   any query of the chunk can see. Its segments, in position order, are
+ *     (0, L) when R0 <= min(S, L);  (R0, L - R0) when S == 0;  else (0, S) and (R0, L - R0).
+ *   A GLOBAL head has the single segment (0, L). L == 0 stores nothing.
+ * - seg_table int32 [B][Hkv][2][4] = {pos_start, n_tok, vpage_start, n_pages} per segment
+ *   slot; an unused slot is {0, 0, running page total, 0}.
+ * - Each segment starts on a fresh page; slot i of the segment's k-th page holds position
+ *   pos_start + k*page_size + i. n_pages = ceil(n_tok / page_size).
+ * - Virtual pages are numbered in (request, head, segment) order from 0; v2p[v] is the
+ *   physical page of virtual page v, taken from the caller's free list in order.
+ * - kv_len int32 [B][Hkv] = number of stored tokens of the head (its true KV length).
+ * - Pools: [n_phys][page_size][D] elements; tail slots of a segment's last page are left
+ *   untouched and never read.
+ */
+#ifndef SEGPAGED_H
+#define SEGPAGED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sp_status {
+  SP_OK = 0,
+  SP_ERR_INVALID_ARG = -1,         /* null pointer, negative size, inconsistent lengths  */
+  SP_ERR_UNSUPPORTED = -2,         /* D, page size, dtype or G outside the supported set */
+  SP_ERR_POOL_TOO_SMALL = -3,      /* fewer free pages than the layout needs             */
+  SP_ERR_WORKSPACE_TOO_SMALL = -4, /* ws_bytes below what the workspace query returned   */
+  SP_ERR_HIP = -5,                 /* a HIP runtime call failed                          */
+  SP_ERR_PLAN_MISMATCH = -6        /* workspace holds no plan for these arguments        */
+} sp_status;
+
+typedef enum sp_dtype { SP_BF16 = 0, SP_F32 = 1 } sp_dtype;
+
+typedef enum sp_head_kind { SP_GLOBAL = 0, SP_LOCAL = 1 } sp_head_kind;
+
+/* One per KV head (page "RedKnot head classification": head types, defaults window 512 and
+ * sink 4). `sink` and `window` are ignored for SP_GLOBAL heads. */
+typedef struct sp_head_policy {
+  int32_t kind;   /* sp_head_kind */
+  int32_t sink;   /* S >= 0       */
+  int32_t window; /* W >= 1       */
+} sp_head_policy;
+
+/* Human-readable name of a status code. Never NULL. */
+const char* segpaged_status_string(int status);
+
+/* Pages the layout needs (the n_virt of segpaged_build). Host only; touches no GPU.
+ * ctx_len, q_len: host [B]; pol: host [Hkv]. Writes *n_pages_needed on success. */
+sp_status segpaged_plan_pages(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                              int32_t Hkv, const sp_head_policy* pol, int32_t page_size,
+                              int64_t* n_pages_needed);
+
+/* Host copy of the tables segpaged_build writes (same rules, no GPU touched).
+ *   seg_table: host int32 [B][Hkv][2][4]; kv_len: host int32 [B][Hkv]. */
+sp_status segpaged_layout_tables(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                                 int32_t Hkv, const sp_head_policy* pol, int32_t page_size,
+                                 int32_t* seg_table, int32_t* kv_len);
+
+/* Build the per-head page tables and fill the pool (page "RedKnot SegPagedAttention runtime
+ * design", section 3: building per-head storage from dense KV keeps only the tokens each
+ * LOCAL head can see; section 5: the layout is built once at KV-write time and reused).
+ *   k_dense, v_dense : device [sum(ctx_len)][Hkv][D]
+ *   free_pages       : host [n_free], distinct ids in [0, n_phys); the first n_virt are used
+ *   k_pool, v_pool   : device [n_phys][page_size][D]
+ *   seg_table        : device int32 [B][Hkv][2][4]   (written)
+ *   kv_len           : device int32 [B][Hkv]         (written)
+ *   v2p              : device int32 [n_virt]         (written; n_virt = segpaged_plan_pages)
+ * The tables are uploaded with a copy that completes before return; the scatter kernel runs
+ * asynchronously on `stream`. Errors: SP_ERR_POOL_TOO_SMALL if n_free < n_virt,
+ * SP_ERR_INVALID_ARG for duplicate or out-of-range free-list entries. */
+sp_status segpaged_build(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int32_t page_size,
+                         const int32_t* ctx_len, const int32_t* q_len, const sp_head_policy* pol,
+                         const void* k_dense, const void* v_dense,
+                         const int32_t* free_pages, int64_t n_free, int64_t n_phys,
+                         void* k_pool, void* v_pool,
+                         int32_t* seg_table, int32_t* kv_len, int32_t* v2p, hipStream_t stream);
+
+/* Bytes of device workspace segpaged_attention needs for these arguments (host only). The
+ * workspace holds the work list (one item per (request, KV head, query block, KV split),
+ * per-XCD queues and counters) and the fp32 partial results of KV-split items. */
+sp_status segpaged_attention_workspace_size(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                            int32_t D, int32_t page_size,
+                                            const int32_t* ctx_len, const int32_t* q_len,
+                                            const sp_head_policy* pol, size_t* bytes);
+
+/* Plan the attention launch into `workspace` (device, >= the size above). The work list
+ * balances long GLOBAL-head tiles against short LOCAL-head tiles: long tiles are split along
+ * KV, items are grouped by KV head onto per-XCD queues and ordered longest first. Done once
+ * per layout (page "RedKnot SegPagedAttention runtime design", section 5: recomputing layout
+ * work on every attention call costs more than it saves). Synchronous: the plan is in place
+ * when this returns. */
+sp_status segpaged_attention_plan(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t page_size, const int32_t* ctx_len,
+                                  const int32_t* q_len, const sp_head_policy* pol,
+                                  void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* O = SegPaged attention (page "RedKnot SegPagedAttention runtime design", section 4: each
+ * head's true KV length comes from its page table; all (query head, KV head) pairs go into
+ * one variable-length launch, each head with its own length).
+ *   q        : device [sum(q_len)][Hq][D]
+ *   k_pool, v_pool, n_phys, seg_table, kv_len, v2p : as written by segpaged_build
+ *   o        : device [sum(q_len)][Hq][D] (written)
+ *   workspace: device, planned by segpaged_attention_plan with the same shape arguments;
+ *              reused across calls (its counters return to zero when the kernels finish).
+ * Query requests with q_len * G <= 16 take the split-KV decode kernel; the others take the
+ * prefill kernel; KV-split items are merged by a fixed-order combine kernel, so O is bitwise
+ * reproducible. Calls that share one workspace must not overlap in time.
+ * Errors: SP_ERR_PLAN_MISMATCH if the workspace was planned for other arguments (checked on
+ * the device; the kernels then write nothing -- see segpaged_attention_check). */
+sp_status segpaged_attention(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                             int32_t page_size, const int32_t* ctx_len, const int32_t* q_len,
+                             const sp_head_policy* pol, const void* q, const void* k_pool,
+                             const void* v_pool, int64_t n_phys, const int32_t* seg_table,
+                             const int32_t* kv_len, const int32_t* v2p, float softmax_scale,
+                             void* o, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Same as segpaged_attention, and records `main_begin` / `main_end` (may be NULL) on
+ * `stream` right before and after the attention kernel(s), before any combine kernel, so a
+ * caller can time the main kernel alone. */
+sp_status segpaged_attention_profiled(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                      int32_t D, int32_t page_size, const int32_t* ctx_len,
+                                      const int32_t* q_len, const sp_head_policy* pol,
+                                      const void* q, const void* k_pool, const void* v_pool,
+                                      int64_t n_phys, const int32_t* seg_table,
+                                      const int32_t* kv_len, const int32_t* v2p,
+                                      float softmax_scale, void* o, void* workspace,
+                                      size_t ws_bytes, hipStream_t stream,
+                                      hipEvent_t main_begin, hipEvent_t main_end);
+
+/* Reads back (synchronising `stream`) the device-side error word of a workspace: SP_OK, or
+ * SP_ERR_PLAN_MISMATCH / SP_ERR_INVALID_ARG if a kernel found a plan for other arguments or a
+ * page id >= n_phys in v2p. Clears the word. */
+sp_status segpaged_attention_check(void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Dense-plus-mask comparison path (page "RedKnot SegPagedAttention runtime design",
+ * sections 4 and 6: the dense + mask baseline the SegPaged result is checked and timed
+ * against). Same tile engine and scheduling, but every head walks its full causal range of
+ * the dense [sum(ctx_len)][Hkv][D] K/V and applies its visibility as an elementwise mask.
+ * Workspace query and plan as above. */
+sp_status segpaged_dense_mask_workspace_size(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                             int32_t D, const int32_t* ctx_len,
+                                             const int32_t* q_len, const sp_head_policy* pol,
+                                             size_t* bytes);
+sp_status segpaged_dense_mask_plan(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                   const int32_t* ctx_len, const int32_t* q_len,
+                                   const sp_head_policy* pol, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream);
+sp_status segpaged_dense_mask_attention(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                        int32_t D, const int32_t* ctx_len, const int32_t* q_len,
+                                        const sp_head_policy* pol, const void* q,
+                                        const void* k_dense, const void* v_dense,
+                                        float softmax_scale, void* o, void* workspace,
+                                        size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEGPAGED_H */

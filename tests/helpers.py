@@ -1,0 +1,76 @@
+"""Shared helpers of the GPU tests: upload seeded inputs, run the library, compare."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from head_aware_paged_segpaged_amd import DenseMaskLayer, SegPagedLayer
+from workloads import free_list
+
+DEV = "cuda:0"
+
+# Parity bar: cosine per (request, query head) > 0.99998 (page "RedKnot SegPagedAttention
+# runtime design", section 4); max-abs 2e-2 for bf16 and 1e-5 for fp32.
+COS_MIN = 0.99998
+MAXABS = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def to_device(x: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def run_segpaged(case, free=None, n_phys=None, scale=None, q_dev=None, kv_dev=None):
+    layer = SegPagedLayer(case.dtype, case.Hq, case.Hkv, case.D, case.P, case.ctx_len,
+                          case.q_len, case.policy, DEV)
+    if free is None:
+        free = free_list(case.seed, layer.n_virt if n_phys is None else n_phys)
+    k, v = kv_dev if kv_dev is not None else (to_device(case.k, case.dtype),
+                                              to_device(case.v, case.dtype))
+    layer.build(k, v, free, n_phys=n_phys)
+    q = q_dev if q_dev is not None else to_device(case.q, case.dtype)
+    out = layer.attention(q, case.scale if scale is None else scale)
+    torch.cuda.synchronize()
+    assert layer.check() == 0, "device-side error word set"
+    return out, layer
+
+
+def run_dense_mask(case, scale=None):
+    layer = DenseMaskLayer(case.dtype, case.Hq, case.Hkv, case.D, case.ctx_len, case.q_len,
+                           case.policy, DEV)
+    k, v = to_device(case.k, case.dtype), to_device(case.v, case.dtype)
+    q = to_device(case.q, case.dtype)
+    out = layer.attention(q, k, v, case.scale if scale is None else scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def compare(got: np.ndarray, ref: np.ndarray, q_len, Hq: int):
+    """(max abs error, min cosine over (request, query head))."""
+    maxabs = float(np.abs(got - ref).max()) if got.size else 0.0
+    cos_min = 1.0
+    q0 = 0
+    for nq in np.asarray(q_len):
+        nq = int(nq)
+        for hq in range(Hq):
+            a = got[q0:q0 + nq, hq, :].ravel()
+            b = ref[q0:q0 + nq, hq, :].ravel()
+            na, nb = np.linalg.norm(a), np.linalg.norm(b)
+            if na == 0 and nb == 0:
+                continue
+            cos_min = min(cos_min, float(a @ b / (na * nb)))
+        q0 += nq
+    return maxabs, cos_min
+
+
+def assert_parity(got: np.ndarray, ref: np.ndarray, case, label=""):
+    maxabs, cos = compare(got, ref, case.q_len, case.Hq)
+    print("%s %s: maxabs=%.3e min_cos=%.8f" % (case.name, label, maxabs, cos), flush=True)
+    assert maxabs <= MAXABS[case.dtype], (label, maxabs)
+    assert cos > COS_MIN, (label, cos)

@@ -1,0 +1,119 @@
+"""CPU tests of the C ABI: the library loads, exports every declared call, its host planner
+matches the page-plan oracle bit-exactly, and invalid calls return their status codes before
+anything touches a GPU."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import head_aware_paged_segpaged_amd as sp
+from head_aware_paged_segpaged_amd import binding
+from oracle import plan_tables
+from workloads import CONFIGS, config_case
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "segpaged.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(segpaged_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_call():
+    lib = sp.lib()
+    declared = _declared()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(binding.EXPORTED) == declared
+
+
+def test_status_strings():
+    for code in range(-6, 1):
+        assert sp.status_string(code)
+    assert "unknown" in sp.status_string(42)
+
+
+@pytest.mark.parametrize("index", range(len(CONFIGS)))
+def test_layout_tables_match_oracle(index):
+    c = config_case(index, with_tensors=False)
+    seg, kvl = sp.segpaged_layout_tables(c.ctx_len, c.q_len, c.policy, c.P)
+    seg_o, kvl_o, n_virt = plan_tables(c.ctx_len, c.q_len, c.policy, c.P)
+    np.testing.assert_array_equal(seg, seg_o)
+    np.testing.assert_array_equal(kvl, kvl_o)
+    assert sp.segpaged_plan_pages(c.ctx_len, c.q_len, c.policy, c.P) == n_virt
+
+
+def test_layout_tables_random_against_oracle():
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        B = int(rng.integers(1, 4))
+        Hkv = int(rng.integers(1, 4))
+        P = int(rng.choice([16, 32, 64, 128, 256]))
+        ctx = rng.integers(0, 700, size=B)
+        q = np.array([rng.integers(0, c + 1) for c in ctx])
+        pol = [(int(rng.integers(0, 2)), int(rng.integers(0, 70)), int(rng.integers(1, 600)))
+               for _ in range(Hkv)]
+        seg, kvl = sp.segpaged_layout_tables(ctx, q, pol, P)
+        seg_o, kvl_o, n_virt = plan_tables(ctx, q, pol, P)
+        np.testing.assert_array_equal(seg, seg_o)
+        np.testing.assert_array_equal(kvl, kvl_o)
+        assert sp.segpaged_plan_pages(ctx, q, pol, P) == n_virt
+
+
+def _err(fn, *a):
+    with pytest.raises(sp.SegPagedError) as e:
+        fn(*a)
+    return e.value.status
+
+
+def test_invalid_arguments_are_rejected_on_the_host():
+    pol = [(1, 4, 64)]
+    E = binding
+    assert _err(sp.segpaged_plan_pages, [10], [11], pol, 16) == E.SP_ERR_INVALID_ARG  # q > L
+    assert _err(sp.segpaged_plan_pages, [10], [-1], pol, 16) == E.SP_ERR_INVALID_ARG
+    assert _err(sp.segpaged_plan_pages, [10], [1], [(1, -1, 4)], 16) == E.SP_ERR_INVALID_ARG
+    assert _err(sp.segpaged_plan_pages, [10], [1], [(1, 2, 0)], 16) == E.SP_ERR_INVALID_ARG
+    assert _err(sp.segpaged_plan_pages, [10], [1], [(7, 2, 3)], 16) == E.SP_ERR_INVALID_ARG
+    assert _err(sp.segpaged_plan_pages, [10], [1], pol, 48) == E.SP_ERR_UNSUPPORTED
+    assert _err(sp.segpaged_plan_pages, [10], [1], pol, 8) == E.SP_ERR_UNSUPPORTED
+    # attention shape checks run before any device query
+    for bad in [dict(D=96), dict(Hq=6, Hkv=4), dict(dtype=7)]:
+        args = dict(dtype="bf16", Hq=8, Hkv=4, D=128)
+        args.update(bad)
+        dtype = args["dtype"]
+        code = binding.lib().segpaged_attention_workspace_size(
+            dtype if isinstance(dtype, int) else 0, 1, args["Hq"], args["Hkv"], args["D"], 64,
+            binding._ptr(np.array([10], np.int32)), binding._ptr(np.array([1], np.int32)),
+            binding._ptr(np.array([(1, 4, 64)] * args["Hkv"], np.int32)),
+            binding.ctypes.byref(binding._sz(0)))
+        assert code in (E.SP_ERR_UNSUPPORTED, E.SP_ERR_INVALID_ARG), bad
+    assert (binding.lib().segpaged_attention_workspace_size(0, 1, 8, 4, 128, 64, None, None,
+                                                             None, None)
+            == E.SP_ERR_INVALID_ARG)
+
+
+def test_build_validates_free_list_before_touching_memory():
+    ctx, q, pol = np.array([100], np.int32), np.array([10], np.int32), [(0, 0, 1)]
+    n_virt = sp.segpaged_plan_pages(ctx, q, pol, 16)
+    assert n_virt == 7
+    lib = binding.lib()
+    c, ql, p = ctx, q, np.array(pol, np.int32)
+    fake = binding._vp(0x1000)  # never dereferenced: validation fails first
+
+    def build(free, n_free, n_phys):
+        fl = np.asarray(free, np.int32)
+        return lib.segpaged_build(0, 1, 1, 128, 16, binding._ptr(c), binding._ptr(ql),
+                                  binding._ptr(p), fake, fake, binding._ptr(fl), n_free, n_phys,
+                                  fake, fake, fake, fake, fake, None)
+
+    assert build(np.arange(6), 6, 6) == binding.SP_ERR_POOL_TOO_SMALL
+    assert build([0, 1, 2, 3, 4, 5, 5], 7, 8) == binding.SP_ERR_INVALID_ARG  # duplicate
+    assert build([0, 1, 2, 3, 4, 5, 9], 7, 8) == binding.SP_ERR_INVALID_ARG  # out of range
+    assert build([0, 1, 2, 3, 4, 5, -1], 7, 8) == binding.SP_ERR_INVALID_ARG
+    assert lib.segpaged_build(0, 1, 1, 96, 16, binding._ptr(c), binding._ptr(ql),
+                              binding._ptr(p), fake, fake, None, 0, 0, fake, fake, fake, fake,
+                              fake, None) == binding.SP_ERR_UNSUPPORTED
