@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     segpaged_attention,
     segpaged_attention_check,
     segpaged_attention_plan,
+    segpaged_attention_plan_host,
     segpaged_attention_profiled,
     segpaged_attention_workspace_size,
     segpaged_build,

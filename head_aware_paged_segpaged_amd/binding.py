@@ -40,6 +40,7 @@ EXPORTED = [
     "segpaged_attention",
     "segpaged_attention_profiled",
     "segpaged_attention_check",
+    "segpaged_attention_plan_host",
     "segpaged_dense_mask_workspace_size",
     "segpaged_dense_mask_plan",
     "segpaged_dense_mask_attention",
@@ -74,6 +75,9 @@ _SIGS = {
                                            _vp, _vp, _vp, _i64, _vp, _vp, _vp, _f, _vp, _vp,
                                            _sz, _vp, _vp, _vp]),
     "segpaged_attention_check": (_i32, [_vp, _sz, _vp]),
+    "segpaged_attention_plan_host": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                            _vp, _i32, _i32, _vp, _sz, ctypes.POINTER(_sz),
+                                            ctypes.POINTER(_sz)]),
     "segpaged_dense_mask_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                                                   ctypes.POINTER(_sz)]),
     "segpaged_dense_mask_plan": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz,
@@ -233,6 +237,23 @@ def segpaged_attention_check(workspace, stream=None) -> int:
     return int(lib().segpaged_attention_check(_dev(workspace, "workspace"),
                                               workspace.numel() * workspace.element_size(),
                                               _stream(stream)))
+
+
+def segpaged_attention_plan_host(dtype, Hq: int, Hkv: int, D: int, page_size: int, ctx_len,
+                                 q_len, policy, slots_prefill: int, slots_decode: int,
+                                 dense_mask: bool = False):
+    """Host copy of the plan bytes (header + work lists) and the workspace size."""
+    c, q, p = _host_i32(ctx_len), _host_i32(q_len), _host_i32(policy).reshape(-1, 3)
+    nb, wb = _sz(0), _sz(0)
+    args = [_dtype_code(dtype), len(c), Hq, Hkv, D, page_size, int(bool(dense_mask)), _ptr(c),
+            _ptr(q), _ptr(p), slots_prefill, slots_decode]
+    _check(lib().segpaged_attention_plan_host(*args, None, 0, ctypes.byref(nb),
+                                              ctypes.byref(wb)), "segpaged_attention_plan_host")
+    buf = np.zeros(nb.value, dtype=np.uint8)
+    _check(lib().segpaged_attention_plan_host(*args, buf.ctypes.data_as(_vp), buf.size,
+                                              ctypes.byref(nb), ctypes.byref(wb)),
+           "segpaged_attention_plan_host")
+    return buf, int(wb.value)
 
 
 def segpaged_dense_mask_workspace_size(dtype, Hq: int, Hkv: int, D: int, ctx_len, q_len,

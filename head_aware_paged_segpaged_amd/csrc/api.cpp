@@ -314,6 +314,30 @@ sp_status segpaged_attention_profiled(sp_dtype dtype, int32_t B, int32_t Hq, int
       main_begin, main_end);
 }
 
+sp_status segpaged_attention_plan_host(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                       int32_t D, int32_t page_size, int32_t dense_mask,
+                                       const int32_t* ctx_len, const int32_t* q_len,
+                                       const sp_head_policy* pol, int32_t slots_prefill,
+                                       int32_t slots_decode, void* host_buf, size_t buf_bytes,
+                                       size_t* plan_bytes, size_t* workspace_bytes) {
+  const Shape s = make_shape(dense_mask ? kModeDense : kModePaged, dtype, B, Hq, Hkv, D,
+                             page_size, ctx_len, q_len, pol);
+  sp_status st = check_shape(s);
+  if (st != SP_OK) return st;
+  if (slots_prefill < 1 || slots_decode < 1 || plan_bytes == nullptr) return SP_ERR_INVALID_ARG;
+  Plan plan;
+  st = make_plan(s, slots_prefill, slots_decode, &plan);
+  if (st != SP_OK) return st;
+  *plan_bytes = plan.upload_bytes;
+  if (workspace_bytes) *workspace_bytes = plan.bytes;
+  if (host_buf == nullptr) return SP_OK;
+  if (buf_bytes < plan.upload_bytes) return SP_ERR_WORKSPACE_TOO_SMALL;
+  std::vector<uint8_t> buf;
+  serialize_plan(plan, &buf);
+  std::memcpy(host_buf, buf.data(), buf.size());
+  return SP_OK;
+}
+
 sp_status segpaged_attention_check(void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (workspace == nullptr || ws_bytes < size_t(kHeaderBytes)) return SP_ERR_INVALID_ARG;
   int32_t word = 0;

@@ -304,10 +304,12 @@ struct KVLoader {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int slot = vt_slot<1, kPrefill>(4 * rg + e);
+          // Reinterpret the whole 16-byte vector, never one extracted element: hipcc (ROCm 7.2)
+          // shrinks a buffer load whose single float-reinterpreted element is used to a
+          // one-dword load of element 0.
+          const f32x4_t fv = __builtin_bit_cast(f32x4_t, vr[j][e]);
 #pragma unroll
-          for (int dd = 0; dd < 4; ++dd) {
-            lv[(dc * 4 + dd) * VS + slot] = __builtin_bit_cast(float, vr[j][e][dd]);
-          }
+          for (int dd = 0; dd < 4; ++dd) lv[(dc * 4 + dd) * VS + slot] = fv[dd];
         }
       }
     }

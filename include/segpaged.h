@@ -177,6 +177,20 @@ sp_status segpaged_attention_profiled(sp_dtype dtype, int32_t B, int32_t Hq, int
                                       size_t ws_bytes, hipStream_t stream,
                                       hipEvent_t main_begin, hipEvent_t main_end);
 
+/* Host-only copy of the plan segpaged_attention_plan (dense_mask = 0) or
+ * segpaged_dense_mask_plan (dense_mask = 1) would upload, for inspection and testing, with the
+ * persistent grid sizes given explicitly instead of read from the current device. Writes
+ * *plan_bytes (bytes of header + work lists) and, if non-NULL, *workspace_bytes; fills
+ * host_buf (buf_bytes >= *plan_bytes) unless it is NULL. Layout of the buffer: a 4096-byte
+ * header, then 64-byte work items and 32-byte combine items, as described in the
+ * library's csrc/sp_common.h. */
+sp_status segpaged_attention_plan_host(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                       int32_t D, int32_t page_size, int32_t dense_mask,
+                                       const int32_t* ctx_len, const int32_t* q_len,
+                                       const sp_head_policy* pol, int32_t slots_prefill,
+                                       int32_t slots_decode, void* host_buf, size_t buf_bytes,
+                                       size_t* plan_bytes, size_t* workspace_bytes);
+
 /* Reads back (synchronising `stream`) the device-side error word of a workspace: SP_OK, or
  * SP_ERR_PLAN_MISMATCH / SP_ERR_INVALID_ARG if a kernel found a plan for other arguments or a
  * page id >= n_phys in v2p. Clears the word. */
