@@ -1,0 +1,299 @@
+"""Benchmark of head-aware SegPaged attention on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I]
+
+One step = one segpaged_attention call (the persistent prefill or decode kernel plus the
+fixed-order combine) over the workload's batch, with the layout already built and the work
+list planned (page "RedKnot SegPagedAttention runtime design", section 5: layout work happens
+once at KV-write time; rebuilding it per call was a slowdown). The build is timed once,
+separately. The same run times this library's dense-plus-mask path on the same inputs and the
+fp64 CPU oracle on a bounded sample of rows, and checks the sampled rows against the oracle.
+
+Prints one JSON line. FLOPs count visible (query, key) pairs only, 4*D per pair; bytes count
+the stored K/V rows once plus Q, O and the page tables.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (matrix and vector)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def visible_counts(case) -> np.ndarray:
+    """Visible (query, key) pairs per (request, KV head), one query head's worth."""
+    out = np.zeros((case.B, case.Hkv), dtype=np.float64)
+    for b in range(case.B):
+        L, nq = int(case.ctx_len[b]), int(case.q_len[b])
+        p = np.arange(L - nq, L, dtype=np.int64)
+        for h in range(case.Hkv):
+            kind, S, W = (int(x) for x in case.policy[h])
+            if kind == 0:
+                n = p + 1
+            else:
+                lo = np.maximum(0, p - W + 1)
+                n = (p - lo + 1) + np.minimum(S, lo)
+            out[b, h] = float(n.sum())
+    return out
+
+
+def stored_rows(case, kv_len) -> float:
+    return float(np.asarray(kv_len, dtype=np.float64).sum())
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "head_aware_paged_segpaged_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    rec = data.get(workload, {}).get(kernel)
+    if not rec or rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_oracle_sample(case, budget_rows: int):
+    """Times the fp64 oracle on a bounded sample of (request, query head) rows."""
+    import oracle
+
+    rng = np.random.default_rng(1234)
+    picks = []
+    for b in range(case.B):
+        nq = int(case.q_len[b])
+        if nq == 0:
+            continue
+        for hq in range(case.Hq):
+            picks.append((b, hq, nq))
+    rng.shuffle(picks)
+    per = max(1, budget_rows // max(1, len(picks)))
+    sample = []
+    rows = 0
+    for b, hq, nq in picks:
+        if rows >= budget_rows:
+            break
+        toks = np.arange(nq) if nq <= per else np.sort(rng.choice(nq, per, replace=False))
+        sample.append((b, hq, toks))
+        rows += len(toks)
+    t0 = time.perf_counter()
+    outs = [oracle.attention_rows(case.q, case.k, case.v, case.ctx_len, case.q_len, case.policy,
+                                  case.Hq, case.Hkv, case.scale, case.dtype, b, hq, toks)
+            for b, hq, toks in sample]
+    secs = time.perf_counter() - t0
+    # visible pairs of the sample
+    G = case.Hq // case.Hkv
+    pairs = 0.0
+    for b, hq, toks in sample:
+        L, nq = int(case.ctx_len[b]), int(case.q_len[b])
+        p = L - nq + toks
+        kind, S, W = (int(x) for x in case.policy[hq // G])
+        if kind == 0:
+            pairs += float((p + 1).sum())
+        else:
+            lo = np.maximum(0, p - W + 1)
+            pairs += float(((p - lo + 1) + np.minimum(S, lo)).sum())
+    return sample, outs, secs, pairs, rows
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1, help="workload index (0-4); default 1")
+    ap.add_argument("--cpu-rows", type=int, default=None,
+                    help="rows of the CPU-oracle sample (default sized for about 10-30 s)")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense+mask timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+
+    from head_aware_paged_segpaged_amd import DenseMaskLayer, HipEvent, SegPagedLayer
+    from workloads import config_case, free_list
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    case = config_case(args.config)
+    t_gen = time.perf_counter() - t_gen
+    print("workload %s generated in %.1f s" % (case.name, t_gen), file=sys.stderr, flush=True)
+
+    def up(x):
+        if case.dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    q, k, v = up(case.q), up(case.k), up(case.v)
+    layer = SegPagedLayer(case.dtype, case.Hq, case.Hkv, case.D, case.P, case.ctx_len, case.q_len,
+                          case.policy, dev)
+    fl = free_list(case.seed, layer.n_virt)
+    stream = torch.cuda.current_stream()
+
+    # Build: timed once, separately (tables upload + scatter kernel).
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    layer.build(k, v, fl)
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t0
+    kv_len = layer.kv_len.cpu().numpy()
+    elem = 2 if case.dtype == "bf16" else 4
+    rows = stored_rows(case, kv_len)
+    build_bytes = 2.0 * 2.0 * rows * case.D * elem  # read + write, K and V
+
+    layer.plan()
+    scale = case.scale
+    out = torch.empty_like(q)
+
+    # Warmup, then K timed steps bracketed by synchronisation; HIP events around the whole
+    # region and around every main (attention) kernel launch.
+    ev_m = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        layer.attention(q, scale, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = HipEvent(), HipEvent()
+    e0.record(stream)
+    for i in range(args.steps):
+        layer.attention(q, scale, out=out, events=ev_m[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_ms(e1)
+    ms_step = total_ms / args.steps
+    main_ms = float(np.mean([a.elapsed_ms(b) for a, b in ev_m]))
+    err = layer.check()
+    assert err == 0, "device-side error %d" % err
+
+    pairs = visible_counts(case).sum() * (case.Hq // case.Hkv)
+    flops = 4.0 * case.D * pairs
+    io_bytes = (2.0 * rows * case.D * elem                      # stored K and V rows
+                + 2.0 * case.tq_total * case.Hq * case.D * elem  # Q and O
+                + layer.seg_table.numel() * 4 + layer.kv_len.numel() * 4 + layer.v2p.numel() * 4)
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    gbps = io_bytes / (ms_step * 1e-3) / 1e9
+    decode = bool((case.q_len * (case.Hq // case.Hkv) <= 16).all())
+    kernel = "decode_kernel" if decode else "prefill_kernel"
+    if decode:
+        achieved = io_bytes / (main_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4)}
+    else:
+        peak = PEAK_BF16_TFLOPS if case.dtype == "bf16" else PEAK_FP32_TFLOPS
+        achieved = flops / (main_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+    roof["kernel"] = kernel
+    roof["kernel_ms"] = round(main_ms, 5)
+    roof["traffic"] = load_traffic(case.name, kernel)
+
+    # Dense + mask baseline on the same inputs.
+    dense = None
+    if not args.no_dense:
+        dl = DenseMaskLayer(case.dtype, case.Hq, case.Hkv, case.D, case.ctx_len, case.q_len,
+                            case.policy, dev)
+        dl.plan()
+        dout = torch.empty_like(q)
+        for _ in range(args.warmup):
+            dl.attention(q, k, v, scale, out=dout)
+        torch.cuda.synchronize()
+        d0, d1 = HipEvent(), HipEvent()
+        d0.record(stream)
+        for _ in range(args.steps):
+            dl.attention(q, k, v, scale, out=dout)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = d0.elapsed_ms(d1) / args.steps
+        dense = {"ms_per_step": round(dense_ms, 5),
+                 "speedup": round(dense_ms / ms_step, 3)}
+
+    # CPU oracle on a bounded sample, and parity of the sampled rows.
+    threads = len(os.sched_getaffinity(0))
+    if args.cpu_rows is None:
+        # the oracle converts one whole (request, KV head) to fp64 per sampled row set, so
+        # decode rows (one per head, contexts up to 128K) are far dearer than prefill rows
+        args.cpu_rows = 256 if int(case.q_len.max()) == 1 else 16384
+    sample, ref_rows, cpu_s, cpu_pairs, cpu_nrows = cpu_oracle_sample(case, args.cpu_rows)
+    got = out.float().cpu().numpy().astype(np.float64)
+    q_row0 = np.concatenate([[0], np.cumsum(case.q_len)[:-1]])
+    maxabs, cos_min = 0.0, 1.0
+    for (b, hq, toks), ref in zip(sample, ref_rows):
+        g = got[q_row0[b] + toks, hq, :]
+        maxabs = max(maxabs, float(np.abs(g - ref).max()))
+        na, nb = np.linalg.norm(g), np.linalg.norm(ref)
+        if na > 0 and nb > 0:
+            cos_min = min(cos_min, float((g.ravel() @ ref.ravel()) / (na * nb)))
+    cpu_tflops = 4.0 * case.D * cpu_pairs / cpu_s / 1e12
+
+    G = case.Hq // case.Hkv
+    dense_tokens = float(np.sum(case.ctx_len)) * case.Hkv
+    line = {
+        "metric": "visible-KV attention TFLOP/s & HBM GB/s (% roofline) + speedup vs dense+mask",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": {"workload": case.name, "B": case.B, "Hq": case.Hq, "Hkv": case.Hkv,
+                   "D": case.D, "page_size": case.P, "ctx_len_total": int(case.ctx_len.sum()),
+                   "q_len_total": int(case.q_len.sum()),
+                   "global_kv_heads": [int(h) for h in np.nonzero(case.policy[:, 0] == 0)[0]],
+                   "local_sink_window": [int(case.policy[:, 1].max()),
+                                         int(case.policy[:, 2].max())],
+                   "gqa_group": G},
+        "gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+        "visible_tflop_per_step": round(flops / 1e12, 6),
+        "roofline": roof,
+        "dense_mask": dense,
+        "speedup_vs_dense_mask": dense["speedup"] if dense else None,
+        "build": {"seconds": round(build_s, 6), "bytes": build_bytes,
+                  "gbps_wall": round(build_bytes / build_s / 1e9, 1)},
+        "kv_savings": round(1.0 - rows / dense_tokens, 4),
+        "parity_sample": {"rows": cpu_nrows, "max_abs": maxabs, "min_cos": cos_min},
+        "cpu_baseline": {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": threads,
+                         "kind": "oracle",
+                         "sample": "%d query rows (%d of %d (request, query head) pairs), "
+                                   "fp64 numpy, %.1f s" % (cpu_nrows, len(sample),
+                                                           case.B * case.Hq, cpu_s)},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

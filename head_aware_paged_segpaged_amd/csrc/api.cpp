@@ -136,7 +136,7 @@ sp_status run_attention(const Shape& s, const void* q, const void* k, const void
   int cus = 0;
   st = device_cus(&cus);
   if (st != SP_OK) return st;
-  if (launch_combine(s.dtype, s.D, 2 * cus, p, stream) != hipSuccess) return SP_ERR_HIP;
+  if (launch_combine(s.dtype, s.D, 4 * cus, p, stream) != hipSuccess) return SP_ERR_HIP;
   return SP_OK;
 }
 

@@ -782,42 +782,52 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
 template <class E, int D>
 __global__ void __launch_bounds__(256) combine_kernel(AttnParams p) {
   using S = typename E::S;
+  constexpr int kTpr = D / 8;                  // threads per row, 8 dims each
+  constexpr int kRowsPerUnit = 256 / kTpr;     // rows merged by one work group pass
+  constexpr int kUnitsPerItem = kTileRows / kRowsPerUnit;
   if (!header_ok(p)) return;
   const WsHeader* hd = reinterpret_cast<const WsHeader*>(p.ws);
   const CombineItem* items = reinterpret_cast<const CombineItem*>(p.ws + hd->off_combine);
   S* obase = static_cast<S*>(p.o);
-  for (int ci = blockIdx.x; ci < hd->n_combine; ci += gridDim.x) {
-    const CombineItem c = items[ci];
+  const int n_units = hd->n_combine * kUnitsPerItem;
+  const int lr = threadIdx.x / kTpr, d0 = (threadIdx.x % kTpr) * 8;
+  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+    const CombineItem c = items[u / kUnitsPerItem];
+    const int r = (u % kUnitsPerItem) * kRowsPerUnit + lr;
+    const int rows = c.nq * p.G;
+    if (r >= rows) continue;
     const int rows_max = c.kind == 0 ? kTileRows : kDecodeRows;
     const float* po = reinterpret_cast<const float*>(p.ws + (c.kind == 0 ? hd->off_part_pre
                                                                         : hd->off_part_dec));
     const float* pm = reinterpret_cast<const float*>(p.ws + (c.kind == 0 ? hd->off_ml_pre
                                                                         : hd->off_ml_dec));
-    const int rows = c.nq * p.G;
-    for (int e = threadIdx.x; e < rows * (D / 4); e += blockDim.x) {
-      const int r = e / (D / 4), d4 = e - r * (D / 4);
-      float M = kNegInf;
-      for (int s = 0; s < c.nsplit; ++s)
-        M = fmaxf(M, pm[(int64_t(c.part0 + s) * rows_max + r) * 2]);
-      const float Mu = M == kNegInf ? 0.f : M;
-      f32x4_t acc = f32x4_t{};
-      float lsum = 0.f;
-      for (int s = 0; s < c.nsplit; ++s) {
-        const int64_t slot = int64_t(c.part0 + s) * rows_max + r;
-        const float f = exp2_fast(pm[slot * 2] - Mu);
-        lsum += f * pm[slot * 2 + 1];
-        acc += f * *reinterpret_cast<const f32x4_t*>(po + slot * D + 4 * d4);
-      }
-      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-      acc *= inv;
-      const int tq = r / p.G, g = r - tq * p.G;
-      const int64_t orow = int64_t(c.q_row0 + c.tq0 + tq) * p.Hq + int64_t(c.h) * p.G + g;
-      if constexpr (sizeof(S) == 2) {
-        u32x2_t v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-        *reinterpret_cast<u32x2_t*>(obase + orow * D + 4 * d4) = v;
-      } else {
-        *reinterpret_cast<f32x4_t*>(obase + orow * D + 4 * d4) = acc;
-      }
+    float M = kNegInf;
+    for (int s = 0; s < c.nsplit; ++s)
+      M = fmaxf(M, pm[(int64_t(c.part0 + s) * rows_max + r) * 2]);
+    const float Mu = M == kNegInf ? 0.f : M;
+    f32x4_t a0 = f32x4_t{}, a1 = f32x4_t{};
+    float lsum = 0.f;
+    for (int s = 0; s < c.nsplit; ++s) {
+      const int64_t slot = int64_t(c.part0 + s) * rows_max + r;
+      const float f = exp2_fast(pm[slot * 2] - Mu);
+      lsum += f * pm[slot * 2 + 1];
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(po + slot * D + d0);
+      a0 += f * src[0];
+      a1 += f * src[1];
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    a0 *= inv;
+    a1 *= inv;
+    const int tq = r / p.G, g = r - tq * p.G;
+    const int64_t orow = int64_t(c.q_row0 + c.tq0 + tq) * p.Hq + int64_t(c.h) * p.G + g;
+    if constexpr (sizeof(S) == 2) {
+      u32x4_t v = {pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]),
+                   pack_bf16x2(a1[0], a1[1]), pack_bf16x2(a1[2], a1[3])};
+      *reinterpret_cast<u32x4_t*>(obase + orow * D + d0) = v;
+    } else {
+      f32x4_t* dst = reinterpret_cast<f32x4_t*>(obase + orow * D + d0);
+      dst[0] = a0;
+      dst[1] = a1;
     }
   }
 }
