@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "launch.h"
 #include "segpaged.h"
 
@@ -105,22 +107,6 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Slot of key kv (0..63) in a V^T row. Prefill (32x32 MFMA): the S^T accumulator register r
-// of lane half hh holds key 8*(r/4) + 4*hh + r%4 of a 32-key block; keys feeding one P*V MFMA
-// are stored side by side so each lane reads them with one access. Decode (16x16 MFMA):
-// lane quad k4 holds keys 4*k4 .. 4*k4+3, the natural order.
-template <int KPL, bool kPrefill>
-__device__ __forceinline__ int vt_slot(int kv) {
-  if constexpr (!kPrefill) {
-    return kv;
-  } else {
-    const int kb = kv >> 5, kl = kv & 31;
-    const int hh = (kl >> 2) & 1;
-    const int r = 4 * (kl >> 3) + (kl & 3);
-    return 32 * kb + (2 * (r / KPL) + hh) * KPL + (r % KPL);
-  }
-}
-
 __device__ __forceinline__ void set_error(uint8_t* ws, int code) {
   atomicCAS(reinterpret_cast<int*>(ws + kOffError), 0, code);
 }
@@ -184,137 +170,83 @@ __device__ __forceinline__ Step describe_step(const WorkItem& w, const ItemKV& k
 }
 
 // ---------------------------------------------------------------------------------------
-// KV step loader: global -> registers (issued one step ahead) -> LDS.
+// LDS tile of one KV step: 64 rows x D elements, row-major, with the 16-byte chunks of a row
+// XOR-swizzled by the row index, so that the same column of 16 consecutive rows lands in 16
+// different bank groups. K and V of a step arrive by LDS-DMA (buffer_load ... lds): each lane
+// of a wave writes 16 bytes at wave_base + 16 * lane, so a lane fetches the source chunk that
+// belongs at its destination slot. No register staging, no ds_write.
 // ---------------------------------------------------------------------------------------
-template <class E, int D, bool kPrefill>
-struct KVLoader {
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <class E, int D>
+struct KVTile {
   using S = typename E::S;
-  static constexpr int kVec = E::kVec;
-  static constexpr int kColsPerRow = D / kVec;              // 16-byte pieces per row
-  static constexpr int kKLoads = (kChunk * kColsPerRow) / 256;
-  static constexpr int kVUnits = 16 * kColsPerRow;          // (4 keys x kVec dims) units
-  static constexpr int kVLoads = (kVUnits + 255) / 256;
-  static constexpr int KS = D + kVec;                       // K row stride (elements)
-  static constexpr int VS = kChunk + kVec;                  // V^T row stride (elements)
-  static constexpr int kKElems = kChunk * KS;
-  static constexpr int kVElems = D * VS;
-  static constexpr uint32_t kOut = 0x80000000u;             // offset past num_records: reads 0
+  static constexpr int kRowBytes = D * int(sizeof(S));
+  static constexpr int kChunks = kRowBytes / 16;           // 16-byte chunks per row
+  static constexpr int kBytes = kChunk * kRowBytes;        // K (or V) of one step
+  static constexpr int kLoads = kChunk * kChunks / 256;    // DMA pieces per thread per tensor
+  static constexpr uint32_t kOut = 0x80000000u;            // offset past num_records: reads 0
 
-  u32x4_t kr[kKLoads];
-  u32x4_t vr[kVLoads][4];
-
-  // V unit u of this thread: 4 consecutive keys 4*rg .. 4*rg+3 and dims dc*kVec ...
-  __device__ __forceinline__ static void v_unit(int u, int& rg, int& dc) {
-    rg = u % 16;
-    dc = u / 16;
+  __device__ __forceinline__ static int swz(int row, int chunk) {
+    return chunk ^ (row & (kChunks - 1));
   }
-
-  // Byte offset of (row, piece col) of the step inside the buffer that starts at `base`.
-  // Loads go through buffer descriptors rebased per step, so every offset is 32-bit and rows
-  // outside the step's valid window read as zero (offset beyond num_records).
-  __device__ __forceinline__ void load(const AttnParams& p, const WorkItem& w, const ItemKV& kv,
-                                       const Step& st, bool dense, uint8_t* ws) {
-    const int tid = threadIdx.x;
-    const S* kbase = static_cast<const S*>(p.k);
-    const S* vbase = static_cast<const S*>(p.v);
-    int64_t off = 0;       // element offset of the descriptor base
-    uint32_t rs = 0;       // row stride in bytes (uniform cases)
-    bool per_row = false;  // small pages: each row looks up its own page
-    int vs = 0;
-    bool uni_ok = true;
-    if (dense) {
-      off = (int64_t(w.kv_row0 + st.ti0) * p.Hkv + w.h) * D;
-      rs = uint32_t(p.Hkv) * D * sizeof(S);
-    } else {
-      vs = st.seg == 0 ? kv.vstart0 : kv.vstart1;
-      if (p.P >= kChunk) {
-        int phys = uniform(p.v2p[vs + st.ti0 / p.P]);
-        if (uint32_t(phys) >= uint64_t(p.n_phys)) {
-          uni_ok = false;
-          phys = 0;
-          if (tid == 0) set_error(ws, SP_ERR_INVALID_ARG);
-        }
-        off = (int64_t(phys) * p.P + (st.ti0 & (p.P - 1))) * D;
-        rs = D * sizeof(S);
-      } else {
-        per_row = true;
-      }
-    }
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), (short)0, 0x7fffffff, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), (short)0, 0x7fffffff, 0x00020000);
-    auto row_off = [&](int row) -> uint32_t {
-      if (!uni_ok || row < st.vlo || row >= st.vhi) return kOut;
-      if (!per_row) return uint32_t(row) * rs;
-      const int ti = st.ti0 + row;
-      const int phys = p.v2p[vs + ti / p.P];
-      if (uint32_t(phys) >= uint64_t(p.n_phys)) return kOut;
-      return uint32_t((phys * p.P + (ti & (p.P - 1))) * D * int(sizeof(S)));
-    };
+  // Byte offset of byte `byte` of row `row` inside a tile.
+  __device__ __forceinline__ static int off(int row, int byte) {
+    return row * kRowBytes + (swz(row, byte >> 4) << 4) + (byte & 15);
+  }
+  // Row and source chunk of this thread's DMA piece j.
+  __device__ __forceinline__ static int piece_row(int j) { return (j * 256 + int(threadIdx.x)) / kChunks; }
+  __device__ __forceinline__ static int piece_chunk(int j) {
+    const int n = j * 256 + int(threadIdx.x);
+    return swz(n / kChunks, n % kChunks);
+  }
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                             0x00020000);
+  }
+  // DMA of the 64 rows of K and V whose first rows start at kb / vb, `rs` bytes apart; rows
+  // outside [vlo, vhi) are written as zero.
+  __device__ __forceinline__ static void dma_strided(const void* kb, const void* vb, uint32_t rs,
+                                                     int vlo, int vhi, bool full, char* lk,
+                                                     char* lv) {
+    const __amdgpu_buffer_rsrc_t rk = rsrc(kb), rv = rsrc(vb);
+    const int wbase = int(threadIdx.x & ~63u) * 16;
 #pragma unroll
-    for (int j = 0; j < kKLoads; ++j) {
-      const int idx = tid + 256 * j;
-      const int row = idx / kColsPerRow, col = idx % kColsPerRow;
-      const uint32_t o = row_off(row);
-      kr[j] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o == kOut ? o : o + col * 16, 0, 0));
-    }
-#pragma unroll
-    for (int j = 0; j < kVLoads; ++j) {
-      int rg, dc;
-      v_unit(tid + 256 * j, rg, dc);
-      const bool unit_ok = tid + 256 * j < kVUnits;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t o = unit_ok ? row_off(4 * rg + e) : kOut;
-        vr[j][e] = __builtin_bit_cast(
-            u32x4_t,
-            __builtin_amdgcn_raw_buffer_load_b128(rv, o == kOut ? o : o + dc * 16, 0, 0));
-      }
+    for (int j = 0; j < kLoads; ++j) {
+      const int row = piece_row(j);
+      uint32_t o = uint32_t(row) * rs + uint32_t(piece_chunk(j)) * 16u;
+      if (!full && (row < vlo || row >= vhi)) o = kOut;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(lk + j * 4096 + wbase), 16, o,
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(lv + j * 4096 + wbase), 16, o,
+                                               0, 0, 0);
     }
   }
-
-  __device__ __forceinline__ void store(S* lk, S* lv) const {
-    const int tid = threadIdx.x;
+  // Pages smaller than a step: every row looks up its own page; offsets are taken from the
+  // pool start (pools under 2 GiB, checked on the host).
+  __device__ __forceinline__ static void dma_small_pages(const AttnParams& p, int vstart, int ti0,
+                                                         int vlo, int vhi, char* lk, char* lv) {
+    const __amdgpu_buffer_rsrc_t rk = rsrc(p.k), rv = rsrc(p.v);
+    const int wbase = int(threadIdx.x & ~63u) * 16;
 #pragma unroll
-    for (int j = 0; j < kKLoads; ++j) {
-      const int idx = tid + 256 * j;
-      const int row = idx / kColsPerRow, col = idx % kColsPerRow;
-      *reinterpret_cast<u32x4_t*>(lk + row * KS + col * kVec) = kr[j];
-    }
-#pragma unroll
-    for (int j = 0; j < kVLoads; ++j) {
-      if (tid + 256 * j >= kVUnits) continue;
-      int rg, dc;
-      v_unit(tid + 256 * j, rg, dc);
-      if constexpr (E::KPL == 8) {
-        // 4 keys x 8 dims -> 8 V^T rows of 4 consecutive slots (8 bytes each).
-        const int slot0 = vt_slot<8, kPrefill>(4 * rg);
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          const int wd = dd >> 1;
-          const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-          u32x2_t o;
-          o[0] = __builtin_amdgcn_perm(vr[j][1][wd], vr[j][0][wd], sel);
-          o[1] = __builtin_amdgcn_perm(vr[j][3][wd], vr[j][2][wd], sel);
-          *reinterpret_cast<u32x2_t*>(lv + (dc * 8 + dd) * VS + slot0) = o;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int slot = vt_slot<1, kPrefill>(4 * rg + e);
-          // Reinterpret the whole 16-byte vector, never one extracted element: hipcc (ROCm 7.2)
-          // shrinks a buffer load whose single float-reinterpreted element is used to a
-          // one-dword load of element 0.
-          const f32x4_t fv = __builtin_bit_cast(f32x4_t, vr[j][e]);
-#pragma unroll
-          for (int dd = 0; dd < 4; ++dd) lv[(dc * 4 + dd) * VS + slot] = fv[dd];
-        }
+    for (int j = 0; j < kLoads; ++j) {
+      const int row = piece_row(j);
+      uint32_t o = kOut;
+      if (row >= vlo && row < vhi) {
+        const int ti = ti0 + row;
+        const int phys = p.v2p[vstart + ti / p.P];
+        if (uint32_t(phys) < uint64_t(p.n_phys))
+          o = uint32_t((phys * p.P + (ti & (p.P - 1))) * kRowBytes + piece_chunk(j) * 16);
       }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(lk + j * 4096 + wbase), 16, o,
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(lv + j * 4096 + wbase), 16, o,
+                                               0, 0, 0);
     }
   }
 };
+
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 __device__ __forceinline__ void load_item_kv(const AttnParams& p, const WorkItem& w, bool dense,
                                              ItemKV& kv, uint8_t* ws) {
@@ -354,6 +286,94 @@ __device__ __forceinline__ bool header_ok(const AttnParams& p) {
   return hd->magic == kMagic && hd->signature == p.signature && hd->bytes <= p.ws_bytes;
 }
 
+// Issues the LDS-DMA of step `st` of item `w` into the tile at lk / lv.
+template <class E, int D, bool kDense>
+__device__ __forceinline__ void issue_step(const AttnParams& p, const WorkItem& w,
+                                           const ItemKV& kv, const Step& st, char* lk, char* lv,
+                                           uint8_t* ws) {
+  using T = KVTile<E, D>;
+  using S = typename E::S;
+  const bool full = st.vlo == 0 && st.vhi == kChunk;
+  if constexpr (kDense) {
+    const int64_t off = (int64_t(w.kv_row0 + st.ti0) * p.Hkv + w.h) * D;
+    T::dma_strided(static_cast<const S*>(p.k) + off, static_cast<const S*>(p.v) + off,
+                   uint32_t(p.Hkv) * T::kRowBytes, st.vlo, st.vhi, full, lk, lv);
+  } else {
+    const int vs = st.seg == 0 ? kv.vstart0 : kv.vstart1;
+    if (p.P >= kChunk) {
+      int phys = uniform(p.v2p[vs + st.ti0 / p.P]);
+      int vlo = st.vlo, vhi = st.vhi;
+      if (uint32_t(phys) >= uint64_t(p.n_phys)) {
+        if (threadIdx.x == 0) set_error(ws, SP_ERR_INVALID_ARG);
+        phys = 0;
+        vlo = vhi = 0;
+      }
+      const int64_t off = (int64_t(phys) * p.P + (st.ti0 & (p.P - 1))) * D;
+      T::dma_strided(static_cast<const S*>(p.k) + off, static_cast<const S*>(p.v) + off,
+                     T::kRowBytes, vlo, vhi, full && vhi > 0, lk, lv);
+    } else {
+      T::dma_small_pages(p, vs, st.ti0, st.vlo, st.vhi, lk, lv);
+    }
+  }
+}
+
+template <class T>
+__device__ __forceinline__ T lds_ld(const char* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+
+// Four bf16 of V transposed by the LDS unit: lane j of each 16-lane group receives element
+// j % 4 of the 8-byte rows addressed by lanes 4e + j / 4 of its group, e = 0..3.
+__device__ __forceinline__ s16x4_t lds_tr4(const char* p) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+}
+
+// Visible keys of one step for one query row, as slot intervals. A step holds positions
+// pos0 .. pos0+63 (slots outside [vlo, vhi) are empty). For a query at p_row the visible slots
+// are those <= p_row - pos0 that are sink positions (< sink) or inside the window
+// (> p_row - window); GLOBAL heads drop the second condition. A step is "dual" when it holds
+// sink positions and may also hold window positions; then two intervals are needed, otherwise
+// one. Intervals are (start, length) and tested as (unsigned)(key - start) < length.
+struct KeyMask {
+  int a0, n0, a1, n1;
+};
+
+__device__ __forceinline__ bool step_is_dual(const Step& st, int kind, int sink, int window,
+                                             int pmin) {
+  return kind != SP_GLOBAL && st.pos0 < sink && st.pos0 + kChunk - 1 > pmin - window;
+}
+
+__device__ __forceinline__ KeyMask key_mask(const Step& st, int p_row, int kind, int sink,
+                                            int window, bool dual, int lane_off) {
+  const int hi = min(st.vhi - 1, p_row - st.pos0);
+  int lo0 = st.vlo, hi0 = hi, lo1 = 1, hi1 = 0;
+  if (kind != SP_GLOBAL) {
+    const int band = p_row - window + 1 - st.pos0;  // first window slot
+    const int sk = sink - st.pos0;                  // first slot past the sink
+    if (dual) {
+      hi0 = min(hi, sk - 1);
+      lo1 = max(st.vlo, band);
+      hi1 = hi;
+    } else if (st.pos0 >= sink) {
+      lo0 = max(st.vlo, band);
+    } else {
+      hi0 = min(hi, sk - 1);
+    }
+  }
+  KeyMask m;
+  m.a0 = lo0 - lane_off;
+  m.n0 = max(0, hi0 - lo0 + 1);
+  m.a1 = lo1 - lane_off;
+  m.n1 = max(0, hi1 - lo1 + 1);
+  return m;
+}
+
+__device__ __forceinline__ bool in_mask(const KeyMask& m, int c, bool dual) {
+  const bool v = uint32_t(c - m.a0) < uint32_t(m.n0);
+  return dual ? (v || uint32_t(c - m.a1) < uint32_t(m.n1)) : v;
+}
+
 // ---------------------------------------------------------------------------------------
 // Prefill: persistent, 256 threads, 128-row tiles.
 // ---------------------------------------------------------------------------------------
@@ -361,15 +381,16 @@ template <class E, int D, int MODE>
 __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     prefill_kernel(AttnParams p) {
   using S = typename E::S;
-  using L = KVLoader<E, D, true>;
+  using T = KVTile<E, D>;
   constexpr int KPL = E::KPL;
-  constexpr int NQK = D / (2 * KPL);   // MFMAs per 32-key block for S^T = K Q^T
-  constexpr int NPV = 16 / KPL;        // MFMAs per 32-key block and 32-dim block for P V
-  constexpr int ND = D / 32;           // 32-dim blocks of O^T
+  constexpr bool kBf16 = KPL == 8;
+  constexpr int NQK = D / (2 * KPL);  // MFMAs per 32-key block for S^T = K Q^T
+  constexpr int ND = D / 32;          // 32-dim blocks of O^T
   constexpr bool kDense = MODE == kModeDense;
+  constexpr int RB = T::kRowBytes;
 
-  __shared__ __attribute__((aligned(16))) S lds_k[2][L::kKElems];
-  __shared__ __attribute__((aligned(16))) S lds_v[2][L::kVElems];
+  // Stage s: K at s * kBytes, V at (2 + s) * kBytes.
+  __shared__ __attribute__((aligned(16))) char lds[4 * T::kBytes];
   __shared__ int s_item;
 
   if (!header_ok(p)) {
@@ -390,6 +411,20 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
   uint32_t exhausted = 0;
   const S* qbase = static_cast<const S*>(p.q);
   S* obase = static_cast<S*>(p.o);
+
+  // Per-lane LDS offsets inside a tile.
+  int kaddr[NQK];  // K fragment c of key row lq (add 32 * RB for the second key block)
+#pragma unroll
+  for (int c = 0; c < NQK; ++c) kaddr[c] = T::off(lq, (2 * KPL * c + KPL * hh) * int(sizeof(S)));
+  int vaddr[2][ND];  // bf16: transposed V reads, half r of the 8 keys of one P*V MFMA
+  if constexpr (kBf16) {
+    const int s = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+        vaddr[r][d] = T::off(8 * r + 4 * (g >> 1) + (s >> 2), 2 * (32 * d + 16 * (g & 1) + 4 * (s & 3)));
+  }
 
   for (;;) {
     if (tid == 0) s_item = pop_item(p.ws, hd->prefill_q, kOffPrefillCnt, xcd, exhausted);
@@ -421,33 +456,51 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     for (int d = 0; d < ND; ++d) oacc[d] = f32x16_t{};
     float m_run = kNegInf, l_run = 0.f;
 
-    L ld;
     const int n = w.c_end - w.c_begin;
     Step cur = describe_step(w, kv, w.c_begin, kDense);
-    ld.load(p, w, kv, cur, kDense, p.ws);
-    ld.store(lds_k[0], lds_v[0]);
+    issue_step<E, D, kDense>(p, w, kv, cur, lds, lds + 2 * T::kBytes, p.ws);
+    wait_dma();
     __syncthreads();
 
-    for (int i = 0; i < n; ++i) {
-      const int stage = i & 1;
+    auto run_step = [&](auto stage_c, int i) {
+      constexpr int stg = decltype(stage_c)::value;
+      const char* lk = lds + stg * T::kBytes;
+      const char* lv = lds + (2 + stg) * T::kBytes;
       const bool has_next = i + 1 < n;
-      Step nxt;
+      Step nxt = cur;
       if (has_next) {
         nxt = describe_step(w, kv, w.c_begin + i + 1, kDense);
-        ld.load(p, w, kv, nxt, kDense, p.ws);
+        issue_step<E, D, kDense>(p, w, kv, nxt, lds + (stg ^ 1) * T::kBytes,
+                                 lds + (2 + (stg ^ 1)) * T::kBytes, p.ws);
       }
-      const S* lk = lds_k[stage];
-      const S* lv = lds_v[stage];
 
       // S^T[key][row] = K Q^T, two 32-key blocks.
-      f32x16_t s[2];
+      f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+      {
+        using F = typename E::Frag;
+        constexpr int kAhead = 2;  // K fragment pairs in flight ahead of the MFMAs
+        F fa[kAhead + 1][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16_t{};
+        for (int c = 0; c < kAhead && c < NQK; ++c) {
+          fa[c][0] = lds_ld<F>(lk + kaddr[c]);
+          fa[c][1] = lds_ld<F>(lk + 32 * RB + kaddr[c]);
+        }
 #pragma unroll
         for (int c = 0; c < NQK; ++c) {
-          const auto a = load_frag<E>(lk + (32 * kb + lq) * L::KS + 2 * KPL * c + KPL * hh);
-          s[kb] = mma32(a, qf[c], s[kb]);
+          if (c + kAhead < NQK) {
+            fa[(c + kAhead) % (kAhead + 1)][0] = lds_ld<F>(lk + kaddr[c + kAhead]);
+            fa[(c + kAhead) % (kAhead + 1)][1] = lds_ld<F>(lk + 32 * RB + kaddr[c + kAhead]);
+          }
+          s0 = mma32(fa[c % (kAhead + 1)][0], qf[c], s0);
+          s1 = mma32(fa[c % (kAhead + 1)][1], qf[c], s1);
+        }
+        if constexpr (kBf16) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+          for (int c = 0; c < NQK; ++c) {
+            if (c + kAhead < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          }
         }
       }
 
@@ -456,38 +509,31 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
       const bool clear = full && last <= pmin &&
                          (kind == SP_GLOBAL || last < sink || cur.pos0 > pmax - window);
       if (kDense || !clear) {
+        const bool dual = step_is_dual(cur, kind, sink, window, pmin);
+        const KeyMask km = key_mask(cur, p_row, kind, sink, window, dual, 4 * hh);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int key = 32 * kb + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-            const int j = cur.pos0 + key;
-            bool ok = key >= cur.vlo && key < cur.vhi && j <= p_row;
-            if (kind != SP_GLOBAL) ok = ok && (j < sink || j > p_row - window);
-            s[kb][rr] = ok ? s[kb][rr] : kNegInf;
-          }
+        for (int rr = 0; rr < 16; ++rr) {
+          const int c = 8 * (rr >> 2) + (rr & 3);
+          s0[rr] = in_mask(km, c, dual) ? s0[rr] : kNegInf;
+          s1[rr] = in_mask(km, 32 + c, dual) ? s1[rr] : kNegInf;
         }
       }
 
       // Online softmax in base 2; row statistics are per lane plus the other lane half.
       float mx = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
+      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, fmaxf(s0[rr], s1[rr]));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx * p.scale_log2);
       const float m_use = m_new == kNegInf ? 0.f : m_new;
       const float alpha = exp2_fast(m_run - m_use);
       float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const float e = exp2_fast(__builtin_fmaf(s[kb][rr], p.scale_log2, -m_use));
-          s[kb][rr] = e;
-          rs += e;
-        }
+      for (int rr = 0; rr < 16; ++rr) {
+        s0[rr] = exp2_fast(__builtin_fmaf(s0[rr], p.scale_log2, -m_use));
+        s1[rr] = exp2_fast(__builtin_fmaf(s1[rr], p.scale_log2, -m_use));
+        rs += s0[rr] + s1[rr];
+      }
       l_run = l_run * alpha + rs;
       m_run = m_new;
       if (__ballot(alpha != 1.f) != 0) {
@@ -496,32 +542,63 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
       }
 
       // O^T[dim][row] += V^T P^T.
+      if constexpr (kBf16) {
+        bf16x8_t pb[2][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int ii = 0; ii < 2; ++ii) {
+          pb[0][ii] = to_bf16x8(s0[8 * ii + 0], s0[8 * ii + 1], s0[8 * ii + 2], s0[8 * ii + 3],
+                                s0[8 * ii + 4], s0[8 * ii + 5], s0[8 * ii + 6], s0[8 * ii + 7]);
+          pb[1][ii] = to_bf16x8(s1[8 * ii + 0], s1[8 * ii + 1], s1[8 * ii + 2], s1[8 * ii + 3],
+                                s1[8 * ii + 4], s1[8 * ii + 5], s1[8 * ii + 6], s1[8 * ii + 7]);
+        }
+        constexpr int kN = 4 * ND;  // P*V MFMAs per step: (key block, half) x dim block
+        constexpr int kAhead = 2;
+        s16x4_t tv[kAhead + 1][2];
+        auto vread = [&](int m, s16x4_t* t) {
+          const int kb = m / (2 * ND), ii = (m / ND) & 1, d = m % ND;
+          const char* base = lv + (32 * kb + 16 * ii) * RB;
+          t[0] = lds_tr4(base + vaddr[0][d]);
+          t[1] = lds_tr4(base + vaddr[1][d]);
+        };
 #pragma unroll
-        for (int ii = 0; ii < NPV; ++ii) {
-          typename E::Frag b;
-          if constexpr (KPL == 8) {
-            b = to_bf16x8(s[kb][8 * ii + 0], s[kb][8 * ii + 1], s[kb][8 * ii + 2],
-                          s[kb][8 * ii + 3], s[kb][8 * ii + 4], s[kb][8 * ii + 5],
-                          s[kb][8 * ii + 6], s[kb][8 * ii + 7]);
-          } else {
-            b = s[kb][ii];
-          }
+        for (int m = 0; m < kAhead; ++m) vread(m, tv[m]);
 #pragma unroll
-          for (int d = 0; d < ND; ++d) {
-            const auto a =
-                load_frag<E>(lv + (32 * d + lq) * L::VS + 32 * kb + (2 * ii + hh) * KPL);
-            oacc[d] = mma32(a, b, oacc[d]);
+        for (int m = 0; m < kN; ++m) {
+          if (m + kAhead < kN) vread(m + kAhead, tv[(m + kAhead) % (kAhead + 1)]);
+          const int kb = m / (2 * ND), ii = (m / ND) & 1, d = m % ND;
+          const s16x4_t* t = tv[m % (kAhead + 1)];
+          const bf16x8_t a = __builtin_bit_cast(
+              bf16x8_t, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[d] = mma32(a, pb[kb][ii], oacc[d]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+        for (int m = 0; m < kN; ++m) {
+          if (m + kAhead < kN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int ii = 0; ii < 16; ++ii) {
+            const int key = 32 * kb + 8 * (ii >> 2) + 4 * hh + (ii & 3);
+            const float b = kb == 0 ? s0[ii] : s1[ii];
+#pragma unroll
+            for (int d = 0; d < ND; ++d) {
+              const float a = lds_ld<float>(lv + T::off(key, 4 * (32 * d + lq)));
+              oacc[d] = mma32(a, b, oacc[d]);
+            }
           }
         }
       }
-
-      if (has_next) {
-        ld.store(lds_k[stage ^ 1], lds_v[stage ^ 1]);
-        cur = nxt;
-      }
+      wait_dma();
       __syncthreads();
+      cur = nxt;
+    };
+    for (int i = 0; i < n; i += 2) {
+      run_step(std::integral_constant<int, 0>{}, i);
+      if (i + 1 < n) run_step(std::integral_constant<int, 1>{}, i + 1);
     }
 
     // Epilogue.
@@ -537,7 +614,7 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
             const int dim = 32 * d + 8 * g4 + 4 * hh;
             const float o0 = oacc[d][4 * g4 + 0] * inv, o1 = oacc[d][4 * g4 + 1] * inv;
             const float o2 = oacc[d][4 * g4 + 2] * inv, o3 = oacc[d][4 * g4 + 3] * inv;
-            if constexpr (KPL == 8) {
+            if constexpr (kBf16) {
               u32x2_t v = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
               *reinterpret_cast<u32x2_t*>(dst + dim) = v;
             } else {
@@ -577,16 +654,16 @@ template <class E, int D, int MODE>
 __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     decode_kernel(AttnParams p) {
   using S = typename E::S;
-  using L = KVLoader<E, D, false>;
-  constexpr int KPL16 = E::KPL == 8 ? 8 : 1;  // reduction elements per lane, 16x16 QK MFMA
-  constexpr int NQK = D / (4 * KPL16);        // MFMAs for one 16-key block
-  constexpr int ND = D / 16;                  // 16-dim blocks of O^T
+  using T = KVTile<E, D>;
+  constexpr bool kBf16 = E::KPL == 8;
+  constexpr int KPL16 = kBf16 ? 8 : 1;  // reduction elements per lane, 16x16 QK MFMA
+  constexpr int NQK = D / (4 * KPL16);  // MFMAs for one 16-key block
+  constexpr int ND = D / 16;            // 16-dim blocks of O^T
   constexpr bool kDense = MODE == kModeDense;
-  static_assert(2 * L::kKElems * sizeof(S) >= 4 * kDecodeRows * D * sizeof(float),
-                "merge scratch fits the K buffers");
+  static_assert(2 * T::kBytes >= 4 * kDecodeRows * D * int(sizeof(float)),
+                "merge scratch fits the K stages");
 
-  __shared__ __attribute__((aligned(16))) S lds_k[2][L::kKElems];
-  __shared__ __attribute__((aligned(16))) S lds_v[2][L::kVElems];
+  __shared__ __attribute__((aligned(16))) char lds[4 * T::kBytes];
   __shared__ float s_ml[4][kDecodeRows][2];
   __shared__ int s_item;
 
@@ -608,7 +685,20 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
   uint32_t exhausted = 0;
   const S* qbase = static_cast<const S*>(p.q);
   S* obase = static_cast<S*>(p.o);
-  float* scratch = reinterpret_cast<float*>(&lds_k[0][0]);
+  float* scratch = reinterpret_cast<float*>(lds);
+
+  int kaddr[NQK];
+#pragma unroll
+  for (int c = 0; c < NQK; ++c)
+    kaddr[c] = T::off(16 * wave + lc, (4 * KPL16 * c + KPL16 * k4) * int(sizeof(S)));
+  int vaddr[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    if constexpr (kBf16)
+      vaddr[d] = T::off(16 * wave + 4 * k4 + (lc >> 2), 2 * (16 * d + 4 * (lc & 3)));
+    else
+      vaddr[d] = 0;
+  }
 
   for (;;) {
     if (tid == 0) s_item = pop_item(p.ws, hd->decode_q, kOffDecodeCnt, xcd, exhausted);
@@ -641,44 +731,39 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     for (int d = 0; d < ND; ++d) oacc[d] = f32x4_t{};
     float m_run = kNegInf, l_run = 0.f;
 
-    L ld;
     const int n = w.c_end - w.c_begin;
     Step cur = describe_step(w, kv, w.c_begin, kDense);
-    ld.load(p, w, kv, cur, kDense, p.ws);
-    ld.store(lds_k[0], lds_v[0]);
+    issue_step<E, D, kDense>(p, w, kv, cur, lds, lds + 2 * T::kBytes, p.ws);
+    wait_dma();
     __syncthreads();
 
-    for (int i = 0; i < n; ++i) {
-      const int stage = i & 1;
+    auto run_step = [&](auto stage_c, int i) {
+      constexpr int stg = decltype(stage_c)::value;
+      const char* lk = lds + stg * T::kBytes;
+      const char* lv = lds + (2 + stg) * T::kBytes;
       const bool has_next = i + 1 < n;
-      Step nxt;
+      Step nxt = cur;
       if (has_next) {
         nxt = describe_step(w, kv, w.c_begin + i + 1, kDense);
-        ld.load(p, w, kv, nxt, kDense, p.ws);
+        issue_step<E, D, kDense>(p, w, kv, nxt, lds + (stg ^ 1) * T::kBytes,
+                                 lds + (2 + (stg ^ 1)) * T::kBytes, p.ws);
       }
-      const S* lk = lds_k[stage];
-      const S* lv = lds_v[stage];
-
       // S^T for keys 16*wave .. 16*wave+15.
       f32x4_t s = f32x4_t{};
 #pragma unroll
       for (int c = 0; c < NQK; ++c) {
-        const auto a = load_frag<E>(lk + (16 * wave + lc) * L::KS + 4 * KPL16 * c + KPL16 * k4);
-        s = mma16(a, qf[c], s);
+        using F = typename E::Frag;
+        s = mma16(lds_ld<F>(lk + kaddr[c]), qf[c], s);
       }
       const bool full = cur.vlo == 0 && cur.vhi == kChunk;
       const int last = cur.pos0 + kChunk - 1;
       const bool clear = full && last <= pmin &&
                          (kind == SP_GLOBAL || last < sink || cur.pos0 > pmax - window);
       if (kDense || !clear) {
+        const bool dual = step_is_dual(cur, kind, sink, window, pmin);
+        const KeyMask km = key_mask(cur, p_row, kind, sink, window, dual, 4 * k4);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int key = 16 * wave + 4 * k4 + rr;
-          const int j = cur.pos0 + key;
-          bool ok = key >= cur.vlo && key < cur.vhi && j <= p_row;
-          if (kind != SP_GLOBAL) ok = ok && (j < sink || j > p_row - window);
-          s[rr] = ok ? s[rr] : kNegInf;
-        }
+        for (int rr = 0; rr < 4; ++rr) s[rr] = in_mask(km, 16 * wave + rr, dual) ? s[rr] : kNegInf;
       }
       float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -689,9 +774,8 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
       float rs = 0.f;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const float e = exp2_fast(__builtin_fmaf(s[rr], p.scale_log2, -m_use));
-        s[rr] = e;
-        rs += e;
+        s[rr] = exp2_fast(__builtin_fmaf(s[rr], p.scale_log2, -m_use));
+        rs += s[rr];
       }
       l_run = l_run * alpha + rs;
       m_run = m_new;
@@ -700,31 +784,31 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
         for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
       }
       // O^T[dim][row] += V^T P^T over this wave's 16 keys.
-      if constexpr (E::KPL == 8) {
+      if constexpr (kBf16) {
         const s16x4_t b = __builtin_bit_cast(
             s16x4_t, u32x2_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])});
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          const s16x4_t a = *reinterpret_cast<const s16x4_t*>(lv + (16 * d + lc) * L::VS +
-                                                              16 * wave + 4 * k4);
-          oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, oacc[d], 0, 0, 0);
+          oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_tr4(lv + vaddr[d]), b, oacc[d],
+                                                              0, 0, 0);
         }
       } else {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
 #pragma unroll
           for (int d = 0; d < ND; ++d) {
-            const float a = lv[(16 * d + lc) * L::VS + 16 * wave + 4 * k4 + rr];
+            const float a = lds_ld<float>(lv + T::off(16 * wave + 4 * k4 + rr, 4 * (16 * d + lc)));
             oacc[d] = mma16(a, s[rr], oacc[d]);
           }
         }
       }
-
-      if (has_next) {
-        ld.store(lds_k[stage ^ 1], lds_v[stage ^ 1]);
-        cur = nxt;
-      }
+      wait_dma();
       __syncthreads();
+      cur = nxt;
+    };
+    for (int i = 0; i < n; i += 2) {
+      run_step(std::integral_constant<int, 0>{}, i);
+      if (i + 1 < n) run_step(std::integral_constant<int, 1>{}, i + 1);
     }
 
     // Merge the four waves' partial softmax states through LDS.
@@ -758,7 +842,7 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
       if (w.part < 0) {
         const int64_t orw = int64_t(w.q_row0 + w.tq0 + tq) * p.Hq + int64_t(w.h) * p.G + gq;
         const float val = lsum > 0.f ? acc / lsum : 0.f;
-        if constexpr (E::KPL == 8) {
+        if constexpr (kBf16) {
           obase[orw * D + dim] = uint16_t(pack_bf16x2(val, 0.f) & 0xffffu);
         } else {
           obase[orw * D + dim] = val;
