@@ -187,8 +187,16 @@ struct KVTile {
   static constexpr int kLoads = kChunk * kChunks / 256;    // DMA pieces per thread per tensor
   static constexpr uint32_t kOut = 0x80000000u;            // offset past num_records: reads 0
 
+  // Chunk permutation of row `row`. With 16 chunks per row the XOR key swaps the two 2-bit
+  // halves of row % 16: any 16 consecutive rows get 16 different keys (row-major fragment reads
+  // are conflict-free) and any 4 consecutive rows get keys in 4 different quarters of the row
+  // (the transposed V reads, 4 rows x 64 bytes per half-wave, are conflict-free too).
   __device__ __forceinline__ static int swz(int row, int chunk) {
-    return chunk ^ (row & (kChunks - 1));
+    if constexpr (kChunks == 16) {
+      return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3));
+    } else {
+      return chunk ^ (row & (kChunks - 1));
+    }
   }
   // Byte offset of byte `byte` of row `row` inside a tile.
   __device__ __forceinline__ static int off(int row, int byte) {
