@@ -214,6 +214,7 @@ struct KVTile {
   }
   // DMA of the 64 rows of K and V whose first rows start at kb / vb, `rs` bytes apart; rows
   // outside [vlo, vhi) are written as zero.
+  template <bool kK, bool kV>
   __device__ __forceinline__ static void dma_strided(const void* kb, const void* vb, uint32_t rs,
                                                      int vlo, int vhi, bool full, char* lk,
                                                      char* lv) {
@@ -224,14 +225,17 @@ struct KVTile {
       const int row = piece_row(j);
       uint32_t o = uint32_t(row) * rs + uint32_t(piece_chunk(j)) * 16u;
       if (!full && (row < vlo || row >= vhi)) o = kOut;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(lk + j * 4096 + wbase), 16, o,
-                                               0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(lv + j * 4096 + wbase), 16, o,
-                                               0, 0, 0);
+      if constexpr (kK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(lk + j * 4096 + wbase), 16, o,
+                                                 0, 0, 0);
+      if constexpr (kV)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(lv + j * 4096 + wbase), 16, o,
+                                                 0, 0, 0);
     }
   }
   // Pages smaller than a step: every row looks up its own page; offsets are taken from the
   // pool start (pools under 2 GiB, checked on the host).
+  template <bool kK, bool kV>
   __device__ __forceinline__ static void dma_small_pages(const AttnParams& p, int vstart, int ti0,
                                                          int vlo, int vhi, char* lk, char* lv) {
     const __amdgpu_buffer_rsrc_t rk = rsrc(p.k), rv = rsrc(p.v);
@@ -246,15 +250,41 @@ struct KVTile {
         if (uint32_t(phys) < uint64_t(p.n_phys))
           o = uint32_t((phys * p.P + (ti & (p.P - 1))) * kRowBytes + piece_chunk(j) * 16);
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(lk + j * 4096 + wbase), 16, o,
-                                               0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(lv + j * 4096 + wbase), 16, o,
-                                               0, 0, 0);
+      if constexpr (kK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(lk + j * 4096 + wbase), 16, o,
+                                                 0, 0, 0);
+      if constexpr (kV)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(lv + j * 4096 + wbase), 16, o,
+                                                 0, 0, 0);
     }
   }
 };
 
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// s_waitcnt vmcnt(N): at most N vector-memory operations of this wave still in flight. They
+// complete in issue order, so every operation issued before the last N has landed.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Work-group barrier for the KV pipeline: this wave's LDS reads are done (lgkmcnt 0) and at
+// most N of its DMAs are in flight, then all waves meet. Unlike __syncthreads it carries no
+// release fence, which would drain every in-flight LDS-DMA (vmcnt 0) and defeat the
+// prefetch; the "memory" clobber keeps the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void kv_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Uniform load through the scalar data cache (read-only use): keeps page-table lookups off
+// the vector-memory counter that tracks the KV DMAs.
+__device__ __forceinline__ int scalar_ld(const int32_t* p, int idx) {
+  typedef __attribute__((address_space(4))) const int32_t cint;
+  return ((cint*)(p))[idx];
+}
 
 __device__ __forceinline__ void load_item_kv(const AttnParams& p, const WorkItem& w, bool dense,
                                              ItemKV& kv, uint8_t* ws) {
@@ -295,21 +325,31 @@ __device__ __forceinline__ bool header_ok(const AttnParams& p) {
 }
 
 // Issues the LDS-DMA of step `st` of item `w` into the tile at lk / lv.
-template <class E, int D, bool kDense>
+// An empty step: no rows. Its DMA writes zeros and touches no page table entry; issuing it
+// keeps the count of vector-memory operations per iteration uniform.
+__device__ __forceinline__ Step empty_step() { return Step{0, 0, 0, 0, 0}; }
+
+// Issues the LDS-DMA of K (kK) and/or V (kV) of step `st` of item `w` into lk / lv.
+template <class E, int D, bool kDense, bool kK, bool kV>
 __device__ __forceinline__ void issue_step(const AttnParams& p, const WorkItem& w,
                                            const ItemKV& kv, const Step& st, char* lk, char* lv,
                                            uint8_t* ws) {
   using T = KVTile<E, D>;
   using S = typename E::S;
+  if (st.vhi <= st.vlo) {
+    T::template dma_strided<kK, kV>(p.k, p.v, 0, 0, 0, false, lk, lv);
+    return;
+  }
   const bool full = st.vlo == 0 && st.vhi == kChunk;
   if constexpr (kDense) {
     const int64_t off = (int64_t(w.kv_row0 + st.ti0) * p.Hkv + w.h) * D;
-    T::dma_strided(static_cast<const S*>(p.k) + off, static_cast<const S*>(p.v) + off,
-                   uint32_t(p.Hkv) * T::kRowBytes, st.vlo, st.vhi, full, lk, lv);
+    T::template dma_strided<kK, kV>(static_cast<const S*>(p.k) + off,
+                                    static_cast<const S*>(p.v) + off,
+                                    uint32_t(p.Hkv) * T::kRowBytes, st.vlo, st.vhi, full, lk, lv);
   } else {
     const int vs = st.seg == 0 ? kv.vstart0 : kv.vstart1;
     if (p.P >= kChunk) {
-      int phys = uniform(p.v2p[vs + st.ti0 / p.P]);
+      int phys = scalar_ld(p.v2p, uniform(vs + st.ti0 / p.P));
       int vlo = st.vlo, vhi = st.vhi;
       if (uint32_t(phys) >= uint64_t(p.n_phys)) {
         if (threadIdx.x == 0) set_error(ws, SP_ERR_INVALID_ARG);
@@ -317,10 +357,11 @@ __device__ __forceinline__ void issue_step(const AttnParams& p, const WorkItem& 
         vlo = vhi = 0;
       }
       const int64_t off = (int64_t(phys) * p.P + (st.ti0 & (p.P - 1))) * D;
-      T::dma_strided(static_cast<const S*>(p.k) + off, static_cast<const S*>(p.v) + off,
-                     T::kRowBytes, vlo, vhi, full && vhi > 0, lk, lv);
+      T::template dma_strided<kK, kV>(static_cast<const S*>(p.k) + off,
+                                      static_cast<const S*>(p.v) + off, T::kRowBytes, vlo, vhi,
+                                      full && vhi > 0, lk, lv);
     } else {
-      T::dma_small_pages(p, vs, st.ti0, st.vlo, st.vhi, lk, lv);
+      T::template dma_small_pages<kK, kV>(p, vs, st.ti0, st.vlo, st.vhi, lk, lv);
     }
   }
 }
@@ -397,8 +438,12 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
   constexpr bool kDense = MODE == kModeDense;
   constexpr int RB = T::kRowBytes;
 
-  // Stage s: K at s * kBytes, V at (2 + s) * kBytes.
-  __shared__ __attribute__((aligned(16))) char lds[4 * T::kBytes];
+  // Two K and two V stages as four separate objects, so that the compiler can tell an LDS
+  // read of one stage from a DMA into another and does not wait for the DMA.
+  __shared__ __attribute__((aligned(16))) char lk0[T::kBytes];
+  __shared__ __attribute__((aligned(16))) char lk1[T::kBytes];
+  __shared__ __attribute__((aligned(16))) char lv0[T::kBytes];
+  __shared__ __attribute__((aligned(16))) char lv1[T::kBytes];
   __shared__ int s_item;
 
   if (!header_ok(p)) {
@@ -464,23 +509,19 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     for (int d = 0; d < ND; ++d) oacc[d] = f32x16_t{};
     float m_run = kNegInf, l_run = 0.f;
 
+    // KV pipeline over the item's steps (stage j & 1 holds step j): K and V of step i+1 are in
+    // flight while step i is computed; one barrier per step.
     const int n = w.c_end - w.c_begin;
     Step cur = describe_step(w, kv, w.c_begin, kDense);
-    issue_step<E, D, kDense>(p, w, kv, cur, lds, lds + 2 * T::kBytes, p.ws);
-    wait_dma();
-    __syncthreads();
+    issue_step<E, D, kDense, true, true>(p, w, kv, cur, lk0, lv0, p.ws);
+    kv_barrier<0>();
 
     auto run_step = [&](auto stage_c, int i) {
       constexpr int stg = decltype(stage_c)::value;
-      const char* lk = lds + stg * T::kBytes;
-      const char* lv = lds + (2 + stg) * T::kBytes;
-      const bool has_next = i + 1 < n;
-      Step nxt = cur;
-      if (has_next) {
-        nxt = describe_step(w, kv, w.c_begin + i + 1, kDense);
-        issue_step<E, D, kDense>(p, w, kv, nxt, lds + (stg ^ 1) * T::kBytes,
-                                 lds + (2 + (stg ^ 1)) * T::kBytes, p.ws);
-      }
+      const char* lk = stg ? lk1 : lk0;
+      const char* lv = stg ? lv1 : lv0;
+      const Step nxt = i + 1 < n ? describe_step(w, kv, w.c_begin + i + 1, kDense) : empty_step();
+      issue_step<E, D, kDense, true, true>(p, w, kv, nxt, stg ? lk0 : lk1, stg ? lv0 : lv1, p.ws);
 
       // S^T[key][row] = K Q^T, two 32-key blocks.
       f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
@@ -600,8 +641,7 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
           }
         }
       }
-      wait_dma();
-      __syncthreads();
+      kv_barrier<0>();  // step i+1 has landed; stage stg is free
       cur = nxt;
     };
     for (int i = 0; i < n; i += 2) {
@@ -668,10 +708,13 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
   constexpr int NQK = D / (4 * KPL16);  // MFMAs for one 16-key block
   constexpr int ND = D / 16;            // 16-dim blocks of O^T
   constexpr bool kDense = MODE == kModeDense;
-  static_assert(2 * T::kBytes >= 4 * kDecodeRows * D * int(sizeof(float)),
-                "merge scratch fits the K stages");
+  static_assert(T::kBytes >= 2 * kDecodeRows * D * int(sizeof(float)),
+                "merge scratch of two waves fits one K stage");
 
-  __shared__ __attribute__((aligned(16))) char lds[4 * T::kBytes];
+  __shared__ __attribute__((aligned(16))) char lk0[T::kBytes];
+  __shared__ __attribute__((aligned(16))) char lk1[T::kBytes];
+  __shared__ __attribute__((aligned(16))) char lv0[T::kBytes];
+  __shared__ __attribute__((aligned(16))) char lv1[T::kBytes];
   __shared__ float s_ml[4][kDecodeRows][2];
   __shared__ int s_item;
 
@@ -693,7 +736,10 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
   uint32_t exhausted = 0;
   const S* qbase = static_cast<const S*>(p.q);
   S* obase = static_cast<S*>(p.o);
-  float* scratch = reinterpret_cast<float*>(lds);
+  // Merge scratch: waves 0-1 use K stage 0, waves 2-3 K stage 1 (both idle by then).
+  auto scratch = [&](int ww, int q) -> float* {
+    return reinterpret_cast<float*>(ww < 2 ? lk0 : lk1) + ((ww & 1) * kDecodeRows + q) * D;
+  };
 
   int kaddr[NQK];
 #pragma unroll
@@ -739,23 +785,24 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     for (int d = 0; d < ND; ++d) oacc[d] = f32x4_t{};
     float m_run = kNegInf, l_run = 0.f;
 
+    // KV pipeline over the item's steps (stage j & 1 holds step j). V(i+1) is issued at the
+    // start of iteration i, K(i+2) right after S^T(i) has been read out of its stage, so each
+    // DMA has about one and a half iterations to land. Every iteration issues exactly one K
+    // and one V transfer (empty past the end), which keeps the vmcnt bookkeeping uniform.
+    constexpr int kDmaOps = T::kLoads;  // vector-memory operations per K or V transfer
     const int n = w.c_end - w.c_begin;
     Step cur = describe_step(w, kv, w.c_begin, kDense);
-    issue_step<E, D, kDense>(p, w, kv, cur, lds, lds + 2 * T::kBytes, p.ws);
-    wait_dma();
+    Step nxt = n > 1 ? describe_step(w, kv, w.c_begin + 1, kDense) : empty_step();
+    issue_step<E, D, kDense, true, true>(p, w, kv, cur, lk0, lv0, p.ws);
+    issue_step<E, D, kDense, true, false>(p, w, kv, nxt, lk1, nullptr, p.ws);
+    wait_vm<0>();
     __syncthreads();
 
     auto run_step = [&](auto stage_c, int i) {
       constexpr int stg = decltype(stage_c)::value;
-      const char* lk = lds + stg * T::kBytes;
-      const char* lv = lds + (2 + stg) * T::kBytes;
-      const bool has_next = i + 1 < n;
-      Step nxt = cur;
-      if (has_next) {
-        nxt = describe_step(w, kv, w.c_begin + i + 1, kDense);
-        issue_step<E, D, kDense>(p, w, kv, nxt, lds + (stg ^ 1) * T::kBytes,
-                                 lds + (2 + (stg ^ 1)) * T::kBytes, p.ws);
-      }
+      const char* lk = stg ? lk1 : lk0;
+      const char* lv = stg ? lv1 : lv0;
+      issue_step<E, D, kDense, false, true>(p, w, kv, nxt, nullptr, stg ? lv0 : lv1, p.ws);
       // S^T for keys 16*wave .. 16*wave+15.
       f32x4_t s = f32x4_t{};
 #pragma unroll
@@ -763,6 +810,10 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
         using F = typename E::Frag;
         s = mma16(lds_ld<F>(lk + kaddr[c]), qf[c], s);
       }
+      kv_barrier<2 * kDmaOps>();
+      const Step nn = i + 2 < n ? describe_step(w, kv, w.c_begin + i + 2, kDense) : empty_step();
+      issue_step<E, D, kDense, true, false>(p, w, kv, nn, stg ? lk1 : lk0, nullptr, p.ws);
+
       const bool full = cur.vlo == 0 && cur.vhi == kChunk;
       const int last = cur.pos0 + kChunk - 1;
       const bool clear = full && last <= pmin &&
@@ -810,14 +861,15 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
           }
         }
       }
-      wait_dma();
-      __syncthreads();
+      kv_barrier<2 * kDmaOps>();
       cur = nxt;
+      nxt = nn;
     };
     for (int i = 0; i < n; i += 2) {
       run_step(std::integral_constant<int, 0>{}, i);
       if (i + 1 < n) run_step(std::integral_constant<int, 1>{}, i + 1);
     }
+    wait_vm<0>();
 
     // Merge the four waves' partial softmax states through LDS.
     float l_w = l_run + __shfl_xor(l_run, 16);
@@ -826,7 +878,7 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     for (int d = 0; d < ND; ++d)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
-        scratch[(wave * kDecodeRows + lc) * D + 16 * d + 4 * k4 + rr] = oacc[d][rr];
+        scratch(wave, lc)[16 * d + 4 * k4 + rr] = oacc[d][rr];
     if (k4 == 0) {
       s_ml[wave][lc][0] = m_run;
       s_ml[wave][lc][1] = l_w;
@@ -843,7 +895,7 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
 #pragma unroll
       for (int ww = 0; ww < 4; ++ww) {
         const float f = exp2_fast(s_ml[ww][q][0] - Mu);
-        acc += f * scratch[(ww * kDecodeRows + q) * D + dim];
+        acc += f * scratch(ww, q)[dim];
         lsum += f * s_ml[ww][q][1];
       }
       const int tq = q / p.G, gq = q - tq * p.G;
