@@ -509,97 +509,102 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     for (int d = 0; d < ND; ++d) oacc[d] = f32x16_t{};
     float m_run = kNegInf, l_run = 0.f;
 
-    // KV pipeline over the item's steps (stage j & 1 holds step j): K and V of step i+1 are in
-    // flight while step i is computed; one barrier per step.
-    const int n = w.c_end - w.c_begin;
-    Step cur = describe_step(w, kv, w.c_begin, kDense);
-    issue_step<E, D, kDense, true, true>(p, w, kv, cur, lk0, lv0, p.ws);
-    kv_barrier<0>();
-
-    auto run_step = [&](auto stage_c, int i) {
-      constexpr int stg = decltype(stage_c)::value;
-      const char* lk = stg ? lk1 : lk0;
-      const char* lv = stg ? lv1 : lv0;
-      const Step nxt = i + 1 < n ? describe_step(w, kv, w.c_begin + i + 1, kDense) : empty_step();
-      issue_step<E, D, kDense, true, true>(p, w, kv, nxt, stg ? lk0 : lk1, stg ? lv0 : lv1, p.ws);
-
-      // S^T[key][row] = K Q^T, two 32-key blocks.
-      f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
-      {
-        using F = typename E::Frag;
-        constexpr int kAhead = 2;  // K fragment pairs in flight ahead of the MFMAs
-        F fa[kAhead + 1][2];
+    // Software pipeline over the item's KV steps. Iteration i runs S^T of step i on the
+    // matrix cores alongside the softmax of step i-1 on the vector ALUs (independent work in
+    // one instruction stream), then P*V of step i-1. K(i+1) and V(i) are in flight during
+    // iteration i; K stage j & 1 holds K(j), V stage j & 1 holds V(j). One barrier per step.
+    using F = typename E::Frag;
+    auto qk = [&](const char* lk, f32x16_t& a0, f32x16_t& a1) {
+      a0 = f32x16_t{};
+      a1 = f32x16_t{};
+      constexpr int kAhead = 2;  // K fragment pairs in flight ahead of the MFMAs
+      F fa[kAhead + 1][2];
 #pragma unroll
-        for (int c = 0; c < kAhead && c < NQK; ++c) {
-          fa[c][0] = lds_ld<F>(lk + kaddr[c]);
-          fa[c][1] = lds_ld<F>(lk + 32 * RB + kaddr[c]);
-        }
-#pragma unroll
-        for (int c = 0; c < NQK; ++c) {
-          if (c + kAhead < NQK) {
-            fa[(c + kAhead) % (kAhead + 1)][0] = lds_ld<F>(lk + kaddr[c + kAhead]);
-            fa[(c + kAhead) % (kAhead + 1)][1] = lds_ld<F>(lk + 32 * RB + kaddr[c + kAhead]);
-          }
-          s0 = mma32(fa[c % (kAhead + 1)][0], qf[c], s0);
-          s1 = mma32(fa[c % (kAhead + 1)][1], qf[c], s1);
-        }
-        if constexpr (kBf16) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
-#pragma unroll
-          for (int c = 0; c < NQK; ++c) {
-            if (c + kAhead < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          }
-        }
+      for (int c = 0; c < kAhead && c < NQK; ++c) {
+        fa[c][0] = lds_ld<F>(lk + kaddr[c]);
+        fa[c][1] = lds_ld<F>(lk + 32 * RB + kaddr[c]);
       }
-
-      const bool full = cur.vlo == 0 && cur.vhi == kChunk;
-      const int last = cur.pos0 + kChunk - 1;
+#pragma unroll
+      for (int c = 0; c < NQK; ++c) {
+        if (c + kAhead < NQK) {
+          fa[(c + kAhead) % (kAhead + 1)][0] = lds_ld<F>(lk + kaddr[c + kAhead]);
+          fa[(c + kAhead) % (kAhead + 1)][1] = lds_ld<F>(lk + 32 * RB + kaddr[c + kAhead]);
+        }
+        a0 = mma32(fa[c % (kAhead + 1)][0], qf[c], a0);
+        a1 = mma32(fa[c % (kAhead + 1)][1], qf[c], a1);
+      }
+    };
+    // Masks step st where it straddles a causal or window edge or is not full.
+    auto mask = [&](const Step& st, f32x16_t& a0, f32x16_t& a1) {
+      const bool full = st.vlo == 0 && st.vhi == kChunk;
+      const int last = st.pos0 + kChunk - 1;
       const bool clear = full && last <= pmin &&
-                         (kind == SP_GLOBAL || last < sink || cur.pos0 > pmax - window);
+                         (kind == SP_GLOBAL || last < sink || st.pos0 > pmax - window);
       if (kDense || !clear) {
-        const bool dual = step_is_dual(cur, kind, sink, window, pmin);
-        const KeyMask km = key_mask(cur, p_row, kind, sink, window, dual, 4 * hh);
+        const bool dual = step_is_dual(st, kind, sink, window, pmin);
+        const KeyMask km = key_mask(st, p_row, kind, sink, window, dual, 4 * hh);
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int c = 8 * (rr >> 2) + (rr & 3);
-          s0[rr] = in_mask(km, c, dual) ? s0[rr] : kNegInf;
-          s1[rr] = in_mask(km, 32 + c, dual) ? s1[rr] : kNegInf;
+          a0[rr] = in_mask(km, c, dual) ? a0[rr] : kNegInf;
+          a1[rr] = in_mask(km, 32 + c, dual) ? a1[rr] : kNegInf;
         }
       }
-
-      // Online softmax in base 2; row statistics are per lane plus the other lane half.
-      float mx = kNegInf;
+    };
+    // Running row maximum: folds step S into m_run, rescales O and l to the new reference
+    // when it moved, and returns the reference the step's exponentials use.
+    auto update_max = [&](const f32x16_t& a0, const f32x16_t& a1) -> float {
+      float m8[8];
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, fmaxf(s0[rr], s1[rr]));
+      for (int t = 0; t < 8; ++t)
+        m8[t] = fmaxf(fmaxf(a0[2 * t], a0[2 * t + 1]), fmaxf(a1[2 * t], a1[2 * t + 1]));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) m8[t] = fmaxf(m8[t], m8[t + 4]);
+      float mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx * p.scale_log2);
       const float m_use = m_new == kNegInf ? 0.f : m_new;
       const float alpha = exp2_fast(m_run - m_use);
-      float rs = 0.f;
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        s0[rr] = exp2_fast(__builtin_fmaf(s0[rr], p.scale_log2, -m_use));
-        s1[rr] = exp2_fast(__builtin_fmaf(s1[rr], p.scale_log2, -m_use));
-        rs += s0[rr] + s1[rr];
-      }
-      l_run = l_run * alpha + rs;
       m_run = m_new;
+      l_run *= alpha;
       if (__ballot(alpha != 1.f) != 0) {
 #pragma unroll
         for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
       }
-
-      // O^T[dim][row] += V^T P^T.
+      return m_use;
+    };
+    // Probabilities of one step against reference m_use: the P operand, and l += row sums.
+    auto probs = [&](f32x16_t& a0, f32x16_t& a1, float m_use, F (&pb)[2][16 / KPL]) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        a0[rr] = exp2_fast(__builtin_fmaf(a0[rr], p.scale_log2, -m_use));
+        a1[rr] = exp2_fast(__builtin_fmaf(a1[rr], p.scale_log2, -m_use));
+      }
+      float r8[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) r8[t] = (a0[2 * t] + a0[2 * t + 1]) + (a1[2 * t] + a1[2 * t + 1]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) r8[t] += r8[t + 4];
+      l_run += (r8[0] + r8[1]) + (r8[2] + r8[3]);
       if constexpr (kBf16) {
-        bf16x8_t pb[2][2];
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
-          pb[0][ii] = to_bf16x8(s0[8 * ii + 0], s0[8 * ii + 1], s0[8 * ii + 2], s0[8 * ii + 3],
-                                s0[8 * ii + 4], s0[8 * ii + 5], s0[8 * ii + 6], s0[8 * ii + 7]);
-          pb[1][ii] = to_bf16x8(s1[8 * ii + 0], s1[8 * ii + 1], s1[8 * ii + 2], s1[8 * ii + 3],
-                                s1[8 * ii + 4], s1[8 * ii + 5], s1[8 * ii + 6], s1[8 * ii + 7]);
+          pb[0][ii] = to_bf16x8(a0[8 * ii + 0], a0[8 * ii + 1], a0[8 * ii + 2], a0[8 * ii + 3],
+                                a0[8 * ii + 4], a0[8 * ii + 5], a0[8 * ii + 6], a0[8 * ii + 7]);
+          pb[1][ii] = to_bf16x8(a1[8 * ii + 0], a1[8 * ii + 1], a1[8 * ii + 2], a1[8 * ii + 3],
+                                a1[8 * ii + 4], a1[8 * ii + 5], a1[8 * ii + 6], a1[8 * ii + 7]);
         }
+      } else {
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+          pb[0][ii] = a0[ii];
+          pb[1][ii] = a1[ii];
+        }
+      }
+    };
+    // O^T[dim][row] += V^T P^T for one step.
+    auto pv = [&](const char* lv, const F (&pb)[2][16 / KPL]) {
+      if constexpr (kBf16) {
         constexpr int kN = 4 * ND;  // P*V MFMAs per step: (key block, half) x dim block
         constexpr int kAhead = 2;
         s16x4_t tv[kAhead + 1][2];
@@ -620,33 +625,65 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
               bf16x8_t, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[d] = mma32(a, pb[kb][ii], oacc[d]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
-#pragma unroll
-        for (int m = 0; m < kN; ++m) {
-          if (m + kAhead < kN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int ii = 0; ii < 16; ++ii) {
             const int key = 32 * kb + 8 * (ii >> 2) + 4 * hh + (ii & 3);
-            const float b = kb == 0 ? s0[ii] : s1[ii];
 #pragma unroll
             for (int d = 0; d < ND; ++d) {
               const float a = lds_ld<float>(lv + T::off(key, 4 * (32 * d + lq)));
-              oacc[d] = mma32(a, b, oacc[d]);
+              oacc[d] = mma32(a, pb[kb][ii], oacc[d]);
             }
           }
         }
       }
-      kv_barrier<0>();  // step i+1 has landed; stage stg is free
+    };
+
+    const int n = w.c_end - w.c_begin;
+    Step prev = describe_step(w, kv, w.c_begin, kDense);
+    Step cur = n > 1 ? describe_step(w, kv, w.c_begin + 1, kDense) : empty_step();
+    // Prologue: S^T, mask and row maximum of step 0; K(1) and V(0) land meanwhile.
+    issue_step<E, D, kDense, true, false>(p, w, kv, prev, lk0, nullptr, p.ws);
+    kv_barrier<0>();
+    issue_step<E, D, kDense, true, false>(p, w, kv, cur, lk1, nullptr, p.ws);
+    issue_step<E, D, kDense, false, true>(p, w, kv, prev, nullptr, lv0, p.ws);
+    f32x16_t sp0, sp1;
+    qk(lk0, sp0, sp1);
+    mask(prev, sp0, sp1);
+    float mp = update_max(sp0, sp1);
+    kv_barrier<0>();
+
+    // Iteration i: (A) S^T(i) on the matrix cores alongside the exponentials of step i-1;
+    // (B) P*V(i-1) alongside the row maximum of step i (after its mask); then O and l move to
+    // the new reference. K(i+1) and V(i) are in flight.
+    auto run_step = [&](auto stage_c, int i) {
+      constexpr int stg = decltype(stage_c)::value;  // i & 1
+      const Step nxt = i + 1 < n ? describe_step(w, kv, w.c_begin + i + 1, kDense) : empty_step();
+      issue_step<E, D, kDense, true, false>(p, w, kv, nxt, stg ? lk0 : lk1, nullptr, p.ws);
+      issue_step<E, D, kDense, false, true>(p, w, kv, cur, nullptr, stg ? lv1 : lv0, p.ws);
+      f32x16_t sc0, sc1;
+      qk(stg ? lk1 : lk0, sc0, sc1);
+      F pb[2][16 / KPL];
+      probs(sp0, sp1, mp, pb);
+      mask(cur, sc0, sc1);
+      pv(stg ? lv0 : lv1, pb);
+      mp = update_max(sc0, sc1);
+      kv_barrier<0>();
+      sp0 = sc0;
+      sp1 = sc1;
       cur = nxt;
     };
-    for (int i = 0; i < n; i += 2) {
-      run_step(std::integral_constant<int, 0>{}, i);
-      if (i + 1 < n) run_step(std::integral_constant<int, 1>{}, i + 1);
+    for (int i = 1; i < n; i += 2) {
+      run_step(std::integral_constant<int, 1>{}, i);
+      if (i + 1 < n) run_step(std::integral_constant<int, 0>{}, i + 1);
+    }
+    {
+      // Last step: its V landed at the final barrier.
+      F pb[2][16 / KPL];
+      probs(sp0, sp1, mp, pb);
+      pv(((n - 1) & 1) ? lv1 : lv0, pb);
     }
 
     // Epilogue.
