@@ -39,6 +39,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
+// Headroom of the prefill softmax reference, in log2 units (exponentials stay <= 2^kSlack).
+constexpr float kSlack = 8.f;
 
 struct BF16 {
   using S = uint16_t;
@@ -219,18 +221,26 @@ struct KVTile {
                                                      int vlo, int vhi, bool full, char* lk,
                                                      char* lv) {
     const __amdgpu_buffer_rsrc_t rk = rsrc(kb), rv = rsrc(vb);
-    const int wbase = int(threadIdx.x & ~63u) * 16;
-#pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      const int row = piece_row(j);
-      uint32_t o = uint32_t(row) * rs + uint32_t(piece_chunk(j)) * 16u;
-      if (!full && (row < vlo || row >= vhi)) o = kOut;
+    const int wbase = uniform(int(threadIdx.x >> 6)) * 1024;
+    auto issue = [&](int j, uint32_t o) {
       if constexpr (kK)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(lk + j * 4096 + wbase), 16, o,
                                                  0, 0, 0);
       if constexpr (kV)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(lv + j * 4096 + wbase), 16, o,
                                                  0, 0, 0);
+    };
+    if (full) {  // uniform: the common case takes no per-row test
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j)
+        issue(j, uint32_t(piece_row(j)) * rs + uint32_t(piece_chunk(j)) * 16u);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) {
+        const int row = piece_row(j);
+        const bool in = row >= vlo && row < vhi;
+        issue(j, in ? uint32_t(row) * rs + uint32_t(piece_chunk(j)) * 16u : kOut);
+      }
     }
   }
   // Pages smaller than a step: every row looks up its own page; offsets are taken from the
@@ -239,7 +249,7 @@ struct KVTile {
   __device__ __forceinline__ static void dma_small_pages(const AttnParams& p, int vstart, int ti0,
                                                          int vlo, int vhi, char* lk, char* lv) {
     const __amdgpu_buffer_rsrc_t rk = rsrc(p.k), rv = rsrc(p.v);
-    const int wbase = int(threadIdx.x & ~63u) * 16;
+    const int wbase = uniform(int(threadIdx.x >> 6)) * 1024;
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       const int row = piece_row(j);
@@ -551,8 +561,11 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
         }
       }
     };
-    // Running row maximum: folds step S into m_run, rescales O and l to the new reference
-    // when it moved, and returns the reference the step's exponentials use.
+    // Softmax reference: m_run is a per-row reference, not the exact running maximum. It
+    // moves (and O and l are rescaled to it) only when some row's maximum passes it by more
+    // than kSlack, so every exponential stays at most 2^kSlack; with logits of ordinary spread
+    // that happens on a row's first steps only, and the O rescale drops out of the loop.
+    // Returns the reference the step's exponentials use.
     auto update_max = [&](const f32x16_t& a0, const f32x16_t& a1) -> float {
       float m8[8];
 #pragma unroll
@@ -561,17 +574,16 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
 #pragma unroll
       for (int t = 0; t < 4; ++t) m8[t] = fmaxf(m8[t], m8[t + 4]);
       float mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * p.scale_log2);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      m_run = m_new;
-      l_run *= alpha;
-      if (__ballot(alpha != 1.f) != 0) {
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
+      if (__ballot(mx > m_run + kSlack) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2_fast(m_run - (m_new == kNegInf ? 0.f : m_new));
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
         for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
       }
-      return m_use;
+      return m_run == kNegInf ? 0.f : m_run;
     };
     // Probabilities of one step against reference m_use: the P operand, and l += row sums.
     auto probs = [&](f32x16_t& a0, f32x16_t& a1, float m_use, F (&pb)[2][16 / KPL]) {
