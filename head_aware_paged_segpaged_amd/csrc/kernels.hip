@@ -145,12 +145,16 @@ struct ItemKV {
   int n_ra;
 };
 
+// One KV step of an item: 64 token slots of one segment. `off` is the element offset of the
+// step's first row in the pool (paged layout, pages of at least one step) or in the dense K/V.
 struct Step {
   int seg, ti0, vlo, vhi, pos0;
+  int64_t off;
 };
 
-__device__ __forceinline__ Step describe_step(const WorkItem& w, const ItemKV& kv, int c,
-                                              bool dense) {
+// Segment, slot range and key positions of step c (no memory access).
+__device__ __forceinline__ Step step_range(const WorkItem& w, const ItemKV& kv, int c,
+                                           bool dense) {
   Step s;
   int base, lo, hi;
   if (c < kv.n_ra) {
@@ -168,6 +172,7 @@ __device__ __forceinline__ Step describe_step(const WorkItem& w, const ItemKV& k
   s.vlo = max(0, lo - s.ti0);
   s.vhi = min(kChunk, hi - s.ti0);
   s.pos0 = dense ? s.ti0 : (s.seg == 0 ? kv.pos0 : kv.pos1) + s.ti0;
+  s.off = 0;
   return s;
 }
 
@@ -296,6 +301,30 @@ __device__ __forceinline__ int scalar_ld(const int32_t* p, int idx) {
   return ((cint*)(p))[idx];
 }
 
+// Step c of item w with its source offset. For pages of at least one step the page-table
+// lookup happens here, once per step, through the scalar cache; a physical page outside the
+// pool flags SP_ERR_INVALID_ARG and the step becomes empty.
+template <int D, bool kDense>
+__device__ __forceinline__ Step describe_step(const AttnParams& p, const WorkItem& w,
+                                              const ItemKV& kv, int c) {
+  Step s = step_range(w, kv, c, kDense);
+  if constexpr (kDense) {
+    s.off = (int64_t(w.kv_row0 + s.ti0) * p.Hkv + w.h) * D;
+  } else {
+    if (p.P >= kChunk && s.vhi > s.vlo) {
+      const int vs = s.seg == 0 ? kv.vstart0 : kv.vstart1;
+      const int phys = scalar_ld(p.v2p, uniform(vs + s.ti0 / p.P));
+      if (uint32_t(phys) >= uint64_t(p.n_phys)) {
+        if (threadIdx.x == 0) set_error(p.ws, SP_ERR_INVALID_ARG);
+        s.vlo = s.vhi = 0;
+      } else {
+        s.off = (int64_t(phys) * p.P + (s.ti0 & (p.P - 1))) * D;
+      }
+    }
+  }
+  return s;
+}
+
 __device__ __forceinline__ void load_item_kv(const AttnParams& p, const WorkItem& w, bool dense,
                                              ItemKV& kv, uint8_t* ws) {
   if (!dense) {
@@ -337,13 +366,12 @@ __device__ __forceinline__ bool header_ok(const AttnParams& p) {
 // Issues the LDS-DMA of step `st` of item `w` into the tile at lk / lv.
 // An empty step: no rows. Its DMA writes zeros and touches no page table entry; issuing it
 // keeps the count of vector-memory operations per iteration uniform.
-__device__ __forceinline__ Step empty_step() { return Step{0, 0, 0, 0, 0}; }
+__device__ __forceinline__ Step empty_step() { return Step{0, 0, 0, 0, 0, 0}; }
 
 // Issues the LDS-DMA of K (kK) and/or V (kV) of step `st` of item `w` into lk / lv.
 template <class E, int D, bool kDense, bool kK, bool kV>
 __device__ __forceinline__ void issue_step(const AttnParams& p, const WorkItem& w,
-                                           const ItemKV& kv, const Step& st, char* lk, char* lv,
-                                           uint8_t* ws) {
+                                           const ItemKV& kv, const Step& st, char* lk, char* lv) {
   using T = KVTile<E, D>;
   using S = typename E::S;
   if (st.vhi <= st.vlo) {
@@ -351,26 +379,16 @@ __device__ __forceinline__ void issue_step(const AttnParams& p, const WorkItem& 
     return;
   }
   const bool full = st.vlo == 0 && st.vhi == kChunk;
+  const S* kb = static_cast<const S*>(p.k) + st.off;
+  const S* vb = static_cast<const S*>(p.v) + st.off;
   if constexpr (kDense) {
-    const int64_t off = (int64_t(w.kv_row0 + st.ti0) * p.Hkv + w.h) * D;
-    T::template dma_strided<kK, kV>(static_cast<const S*>(p.k) + off,
-                                    static_cast<const S*>(p.v) + off,
-                                    uint32_t(p.Hkv) * T::kRowBytes, st.vlo, st.vhi, full, lk, lv);
+    T::template dma_strided<kK, kV>(kb, vb, uint32_t(p.Hkv) * T::kRowBytes, st.vlo, st.vhi, full,
+                                    lk, lv);
   } else {
-    const int vs = st.seg == 0 ? kv.vstart0 : kv.vstart1;
     if (p.P >= kChunk) {
-      int phys = scalar_ld(p.v2p, uniform(vs + st.ti0 / p.P));
-      int vlo = st.vlo, vhi = st.vhi;
-      if (uint32_t(phys) >= uint64_t(p.n_phys)) {
-        if (threadIdx.x == 0) set_error(ws, SP_ERR_INVALID_ARG);
-        phys = 0;
-        vlo = vhi = 0;
-      }
-      const int64_t off = (int64_t(phys) * p.P + (st.ti0 & (p.P - 1))) * D;
-      T::template dma_strided<kK, kV>(static_cast<const S*>(p.k) + off,
-                                      static_cast<const S*>(p.v) + off, T::kRowBytes, vlo, vhi,
-                                      full && vhi > 0, lk, lv);
+      T::template dma_strided<kK, kV>(kb, vb, T::kRowBytes, st.vlo, st.vhi, full, lk, lv);
     } else {
+      const int vs = st.seg == 0 ? kv.vstart0 : kv.vstart1;
       T::template dma_small_pages<kK, kV>(p, vs, st.ti0, st.vlo, st.vhi, lk, lv);
     }
   }
@@ -654,13 +672,18 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     };
 
     const int n = w.c_end - w.c_begin;
-    Step prev = describe_step(w, kv, w.c_begin, kDense);
-    Step cur = n > 1 ? describe_step(w, kv, w.c_begin + 1, kDense) : empty_step();
+    auto step_at = [&](int i) {
+      return i < n ? describe_step<D, kDense>(p, w, kv, w.c_begin + i) : empty_step();
+    };
+    // Steps are described (page lookup included) one iteration before their first DMA.
+    Step prev = step_at(0);
+    Step cur = step_at(1);
+    Step nxt = step_at(2);
     // Prologue: S^T, mask and row maximum of step 0; K(1) and V(0) land meanwhile.
-    issue_step<E, D, kDense, true, false>(p, w, kv, prev, lk0, nullptr, p.ws);
+    issue_step<E, D, kDense, true, false>(p, w, kv, prev, lk0, nullptr);
     kv_barrier<0>();
-    issue_step<E, D, kDense, true, false>(p, w, kv, cur, lk1, nullptr, p.ws);
-    issue_step<E, D, kDense, false, true>(p, w, kv, prev, nullptr, lv0, p.ws);
+    issue_step<E, D, kDense, true, false>(p, w, kv, cur, lk1, nullptr);
+    issue_step<E, D, kDense, false, true>(p, w, kv, prev, nullptr, lv0);
     f32x16_t sp0, sp1;
     qk(lk0, sp0, sp1);
     mask(prev, sp0, sp1);
@@ -672,9 +695,9 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     // the new reference. K(i+1) and V(i) are in flight.
     auto run_step = [&](auto stage_c, int i) {
       constexpr int stg = decltype(stage_c)::value;  // i & 1
-      const Step nxt = i + 1 < n ? describe_step(w, kv, w.c_begin + i + 1, kDense) : empty_step();
-      issue_step<E, D, kDense, true, false>(p, w, kv, nxt, stg ? lk0 : lk1, nullptr, p.ws);
-      issue_step<E, D, kDense, false, true>(p, w, kv, cur, nullptr, stg ? lv1 : lv0, p.ws);
+      issue_step<E, D, kDense, true, false>(p, w, kv, nxt, stg ? lk0 : lk1, nullptr);
+      issue_step<E, D, kDense, false, true>(p, w, kv, cur, nullptr, stg ? lv1 : lv0);
+      const Step nn = step_at(i + 2);
       f32x16_t sc0, sc1;
       qk(stg ? lk1 : lk0, sc0, sc1);
       F pb[2][16 / KPL];
@@ -686,6 +709,7 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
       sp0 = sc0;
       sp1 = sc1;
       cur = nxt;
+      nxt = nn;
     };
     for (int i = 1; i < n; i += 2) {
       run_step(std::integral_constant<int, 1>{}, i);
@@ -840,10 +864,10 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     // and one V transfer (empty past the end), which keeps the vmcnt bookkeeping uniform.
     constexpr int kDmaOps = T::kLoads;  // vector-memory operations per K or V transfer
     const int n = w.c_end - w.c_begin;
-    Step cur = describe_step(w, kv, w.c_begin, kDense);
-    Step nxt = n > 1 ? describe_step(w, kv, w.c_begin + 1, kDense) : empty_step();
-    issue_step<E, D, kDense, true, true>(p, w, kv, cur, lk0, lv0, p.ws);
-    issue_step<E, D, kDense, true, false>(p, w, kv, nxt, lk1, nullptr, p.ws);
+    Step cur = describe_step<D, kDense>(p, w, kv, w.c_begin);
+    Step nxt = n > 1 ? describe_step<D, kDense>(p, w, kv, w.c_begin + 1) : empty_step();
+    issue_step<E, D, kDense, true, true>(p, w, kv, cur, lk0, lv0);
+    issue_step<E, D, kDense, true, false>(p, w, kv, nxt, lk1, nullptr);
     wait_vm<0>();
     __syncthreads();
 
@@ -851,7 +875,7 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
       constexpr int stg = decltype(stage_c)::value;
       const char* lk = stg ? lk1 : lk0;
       const char* lv = stg ? lv1 : lv0;
-      issue_step<E, D, kDense, false, true>(p, w, kv, nxt, nullptr, stg ? lv0 : lv1, p.ws);
+      issue_step<E, D, kDense, false, true>(p, w, kv, nxt, nullptr, stg ? lv0 : lv1);
       // S^T for keys 16*wave .. 16*wave+15.
       f32x4_t s = f32x4_t{};
 #pragma unroll
@@ -860,8 +884,8 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
         s = mma16(lds_ld<F>(lk + kaddr[c]), qf[c], s);
       }
       kv_barrier<2 * kDmaOps>();
-      const Step nn = i + 2 < n ? describe_step(w, kv, w.c_begin + i + 2, kDense) : empty_step();
-      issue_step<E, D, kDense, true, false>(p, w, kv, nn, stg ? lk1 : lk0, nullptr, p.ws);
+      const Step nn = i + 2 < n ? describe_step<D, kDense>(p, w, kv, w.c_begin + i + 2) : empty_step();
+      issue_step<E, D, kDense, true, false>(p, w, kv, nn, stg ? lk1 : lk0, nullptr);
 
       const bool full = cur.vlo == 0 && cur.vhi == kChunk;
       const int last = cur.pos0 + kChunk - 1;
@@ -918,7 +942,10 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
       run_step(std::integral_constant<int, 0>{}, i);
       if (i + 1 < n) run_step(std::integral_constant<int, 1>{}, i + 1);
     }
-    wait_vm<0>();
+    // Every wave's trailing K transfers (zero fills past the last step) target the K stages
+    // that hold the merge scratch below: all of them must have landed before any wave writes
+    // there, so wait for this wave's own and then meet the others.
+    kv_barrier<0>();
 
     // Merge the four waves' partial softmax states through LDS.
     float l_w = l_run + __shfl_xor(l_run, 16);

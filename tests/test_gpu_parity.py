@@ -156,3 +156,20 @@ def test_plan_mismatch_is_reported_not_computed():
     torch.cuda.synchronize()
     assert layer.check() == -6  # SP_ERR_PLAN_MISMATCH
     assert bool((o == 7.0).all())
+
+
+def test_decode_repeat_is_bitwise_identical():
+    # Split-KV decode items merged by the combine kernel in a fixed order: every call of the
+    # same inputs must give the same bits (a cross-wave LDS race would show up here).
+    c = custom_case(42, dtype="bf16", Hq=64, Hkv=8, D=128, P=64,
+                    ctx_len=[4100, 9000, 17000, 700, 64, 5000],
+                    q_len=[1] * 6, policy=[(G_, 0, 1), (G_, 0, 1)] + [(L_, 4, 512)] * 6)
+    print("case decode repeat", flush=True)
+    out, layer = run_segpaged(c)
+    assert_parity(to_f64(out), _oracle(c), c, "decode_repeat")
+    q = to_device(c.q, c.dtype)
+    for _ in range(30):
+        o2 = layer.attention(q, c.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out, o2)
+    assert layer.check() == 0
