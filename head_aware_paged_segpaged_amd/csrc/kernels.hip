@@ -769,30 +769,117 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
 }
 
 // ---------------------------------------------------------------------------------------
-// Decode: persistent, 256 threads, up to 16 rows, split-KV.
+// Decode: persistent, one wave per work group and per work item, up to 16 query rows,
+// split-KV. The wave walks its item in sub-steps of 16 keys; every page size is a multiple
+// of 16, so a sub-step never straddles a page and needs one page-table lookup. K goes from
+// memory straight into registers, already in MFMA operand layout; V goes by LDS-DMA into the
+// wave's own ring of 16-row tiles (read back transposed). Both run kDecAhead sub-steps ahead
+// of the arithmetic. Nothing is shared between waves, so the wave's own vector-memory
+// counter orders every transfer and there is no work-group barrier: decode is bound by how
+// many bytes are in flight, and this keeps several times more of them in flight per CU than
+// a 256-thread tile shared through LDS can.
 // ---------------------------------------------------------------------------------------
-template <class E, int D, int MODE>
-__global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
-    decode_kernel(AttnParams p) {
-  using S = typename E::S;
-  using T = KVTile<E, D>;
-  constexpr bool kBf16 = E::KPL == 8;
-  constexpr int KPL16 = kBf16 ? 8 : 1;  // reduction elements per lane, 16x16 QK MFMA
-  constexpr int NQK = D / (4 * KPL16);  // MFMAs for one 16-key block
-  constexpr int ND = D / 16;            // 16-dim blocks of O^T
-  constexpr bool kDense = MODE == kModeDense;
-  static_assert(T::kBytes >= 2 * kDecodeRows * D * int(sizeof(float)),
-                "merge scratch of two waves fits one K stage");
+constexpr int kSub = 16;      // keys per decode sub-step
+constexpr int kDecAhead = 3;  // sub-steps of K and V in flight ahead of the one computed
 
-  __shared__ __attribute__((aligned(16))) char lk0[T::kBytes];
-  __shared__ __attribute__((aligned(16))) char lk1[T::kBytes];
-  __shared__ __attribute__((aligned(16))) char lv0[T::kBytes];
-  __shared__ __attribute__((aligned(16))) char lv1[T::kBytes];
-  __shared__ float s_ml[4][kDecodeRows][2];
-  __shared__ int s_item;
+// One decode sub-step: rows [vlo, vhi) of 16 are valid; `off` is the element offset of row 0
+// in the pool or the dense K/V (0 when there is no valid row).
+struct Sub {
+  int vlo, vhi, pos0;
+  int64_t off;
+};
+
+// Source of a decode item's two slot ranges (A, then B): first step, valid slot bounds, first
+// virtual page and first key position of each, resolved per item into plain integers. Per
+// sub-step the range is picked arithmetically rather than by a select between fields, which
+// the compiler can turn into a load through a selected address and so into scratch memory.
+struct SubSrc {
+  int n_ra, log2_p;
+  int a_base, a_lo, a_hi, a_vs, a_pos;
+  int b_base, b_lo, b_hi, b_vs, b_pos;
+};
+
+__device__ __forceinline__ SubSrc sub_source(const WorkItem& w, const ItemKV& kv, bool dense,
+                                             int page_size) {
+  SubSrc r;
+  r.n_ra = kv.n_ra;
+  r.log2_p = dense ? 0 : int(__builtin_ctz(uint32_t(page_size)));
+  r.a_base = w.ra_begin / kChunk;
+  r.a_lo = w.ra_begin;
+  r.a_hi = w.ra_end;
+  r.a_vs = w.ra_seg == 0 ? kv.vstart0 : kv.vstart1;
+  r.a_pos = dense ? 0 : (w.ra_seg == 0 ? kv.pos0 : kv.pos1);
+  r.b_base = w.rb_begin / kChunk - kv.n_ra;
+  r.b_lo = w.rb_begin;
+  r.b_hi = w.rb_end;
+  r.b_vs = w.rb_seg == 0 ? kv.vstart0 : kv.vstart1;
+  r.b_pos = dense ? 0 : (w.rb_seg == 0 ? kv.pos0 : kv.pos1);
+  return r;
+}
+
+template <int D, bool kDense>
+__device__ __forceinline__ Sub describe_sub(const AttnParams& p, const WorkItem& w,
+                                            const SubSrc& r, int s) {
+  const int c = w.c_begin + (s >> 2);
+  const int ia = int(c < r.n_ra);  // 1: range A, 0: range B
+  const int base = r.b_base + ia * (r.a_base - r.b_base) + c;
+  const int lo = r.b_lo + ia * (r.a_lo - r.b_lo);
+  const int hi = r.b_hi + ia * (r.a_hi - r.b_hi);
+  const int vs = r.b_vs + ia * (r.a_vs - r.b_vs);
+  const int pos = r.b_pos + ia * (r.a_pos - r.b_pos);
+  const int t0 = base * kChunk + kSub * (s & 3);  // first slot of the sub-step
+  Sub u;
+  u.vlo = min(max(lo - t0, 0), kSub);
+  u.vhi = min(max(hi - t0, 0), kSub);
+  u.pos0 = pos + t0;
+  u.off = 0;
+  if (u.vhi > u.vlo) {
+    if constexpr (kDense) {
+      u.off = (int64_t(w.kv_row0 + t0) * p.Hkv + w.h) * D;
+    } else {
+      const int phys = scalar_ld(p.v2p, uniform(vs + (t0 >> r.log2_p)));
+      if (uint32_t(phys) >= uint64_t(p.n_phys)) {
+        if (__lane_id() == 0) set_error(p.ws, SP_ERR_INVALID_ARG);
+        u.vlo = u.vhi = 0;
+      } else {
+        u.off = ((int64_t(phys) << r.log2_p) + (t0 & (p.P - 1))) * D;
+      }
+    }
+  }
+  return u;
+}
+
+// 16 bytes per lane from a buffer into registers / into LDS at lds + 16 * lane (device-only
+// builtins kept out of the kernel body, which the host pass also parses).
+__device__ __forceinline__ u32x4_t buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void buffer_dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, off, 0, 0, 0);
+}
+
+template <class E, int D, int MODE>
+__global__ void __launch_bounds__(64) decode_kernel(AttnParams p) {
+  using S = typename E::S;
+  using T = KVTile<E, D>;  // same row pitch and chunk swizzle, 16 rows used
+  constexpr bool kBf16 = E::KPL == 8;
+  constexpr bool kDense = MODE == kModeDense;
+  constexpr int kTileBytes = kSub * T::kRowBytes;
+  constexpr int kL = kTileBytes / 1024;  // 16-byte-per-lane transfers per K or V sub-step
+  constexpr int ND = D / 16;             // 16-dim blocks of O^T
+  constexpr int kStages = kDecAhead + 1;
+  static_assert(kL >= 1 && kTileBytes % 1024 == 0, "sub-step tile is whole wave transfers");
+
+  // The V ring as four separate objects: the compiler then tells a transposed read of one
+  // stage from a DMA into another and does not wait for the DMA.
+  __shared__ __attribute__((aligned(16))) char lv0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char lv1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char lv2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char lv3[kTileBytes];
+  auto ring = [&](int i) -> char* { return i == 0 ? lv0 : i == 1 ? lv1 : i == 2 ? lv2 : lv3; };
 
   if (!header_ok(p)) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) set_error(p.ws, SP_ERR_PLAN_MISMATCH);
+    if (__lane_id() == 0 && blockIdx.x == 0) set_error(p.ws, SP_ERR_PLAN_MISMATCH);
     return;
   }
   const WsHeader* hd = reinterpret_cast<const WsHeader*>(p.ws);
@@ -801,40 +888,46 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
   float* part_o = reinterpret_cast<float*>(p.ws + hd->off_part_dec);
   float* part_ml = reinterpret_cast<float*>(p.ws + hd->off_ml_dec);
 
-  const int tid = threadIdx.x;
-  const int wave = uniform(tid >> 6);
-  const int lane = tid & 63;
+  const int lane = __lane_id();
   const int lc = lane & 15, k4 = lane >> 4;
   const int xcd = blockIdx.x % kXcds;
   uint32_t exhausted = 0;
   const S* qbase = static_cast<const S*>(p.q);
   S* obase = static_cast<S*>(p.o);
-  // Merge scratch: waves 0-1 use K stage 0, waves 2-3 K stage 1 (both idle by then).
-  auto scratch = [&](int ww, int q) -> float* {
-    return reinterpret_cast<float*>(ww < 2 ? lk0 : lk1) + ((ww & 1) * kDecodeRows + q) * D;
-  };
+  const uint32_t rs = kDense ? uint32_t(p.Hkv) * T::kRowBytes : uint32_t(T::kRowBytes);
 
-  int kaddr[NQK];
+  // K transfer j of a sub-step: lane (row lc, group k4) fetches bytes [64j + 16k4, +16) of
+  // key row lc. bf16: that is the A operand of 16x16x32 MFMA j (dims 32j + 8k4 .. +7).
+  // fp32: four floats, dims 16j + 4k4 + e, the A operands of 16x16x4 MFMAs 4j + e; the Q
+  // operands below use the same dimension order, so the products sum over every dimension.
+  const uint32_t k_lane = uint32_t(lc) * rs + 16u * uint32_t(k4);
+  // V DMA j: lane writes LDS bytes [1024j + 16 lane, +16) = row (64j + lane) / kChunks, and so
+  // fetches the source chunk the swizzle puts there.
+  uint32_t v_lane[kL];
 #pragma unroll
-  for (int c = 0; c < NQK; ++c)
-    kaddr[c] = T::off(16 * wave + lc, (4 * KPL16 * c + KPL16 * k4) * int(sizeof(S)));
+  for (int j = 0; j < kL; ++j) {
+    const int n = 64 * j + lane;
+    const int row = n / T::kChunks;
+    v_lane[j] = uint32_t(row) * rs + uint32_t(T::swz(row, n % T::kChunks)) * 16u;
+  }
+  // bf16: transposed V reads, one per 16-dim block (see the prefill kernel for the layout).
   int vaddr[ND];
 #pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    if constexpr (kBf16)
-      vaddr[d] = T::off(16 * wave + 4 * k4 + (lc >> 2), 2 * (16 * d + 4 * (lc & 3)));
-    else
-      vaddr[d] = 0;
-  }
+  for (int d = 0; d < ND; ++d)
+    vaddr[d] = kBf16 ? T::off(4 * k4 + (lc >> 2), 2 * (16 * d + 4 * (lc & 3))) : 0;
 
   for (;;) {
-    if (tid == 0) s_item = pop_item(p.ws, hd->decode_q, kOffDecodeCnt, xcd, exhausted);
-    __syncthreads();
-    const int it = uniform(s_item);
+    int it = 0;
+    if (lane == 0) it = pop_item(p.ws, hd->decode_q, kOffDecodeCnt, xcd, exhausted);
+    it = uniform(it);
     if (it < 0) break;
     const WorkItem w = load_item(items, it);
-    ItemKV kv;
-    load_item_kv(p, w, kDense, kv, p.ws);
+    SubSrc src;
+    {
+      ItemKV kv;
+      load_item_kv(p, w, kDense, kv, p.ws);
+      src = sub_source(w, kv, kDense, p.P);
+    }
     const int kind = uniform(pol[w.h * 3 + 0]);
     const int sink = uniform(pol[w.h * 3 + 1]);
     const int window = uniform(pol[w.h * 3 + 2]);
@@ -845,11 +938,16 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     const bool row_ok = lc < rows;
     const int p_row = w.p0 + w.tq0 + tl;
     const int64_t orow = int64_t(w.q_row0 + w.tq0 + tl) * p.Hq + int64_t(w.h) * p.G + g;
-    typename E::Frag qf[NQK];
+    typename E::Frag qf[kBf16 ? kL : 4 * kL];
 #pragma unroll
-    for (int c = 0; c < NQK; ++c) {
-      qf[c] = row_ok ? load_frag<E>(qbase + orow * D + 4 * KPL16 * c + KPL16 * k4)
-                     : zero_frag<E>();
+    for (int j = 0; j < kL; ++j) {
+      if constexpr (kBf16) {
+        qf[j] = row_ok ? load_frag<E>(qbase + orow * D + 32 * j + 8 * k4) : zero_frag<E>();
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          qf[4 * j + e] = row_ok ? load_frag<E>(qbase + orow * D + 16 * j + 4 * k4 + e) : 0.f;
+      }
     }
     const int pmin = w.p0 + w.tq0, pmax = pmin + w.nq - 1;
 
@@ -858,142 +956,142 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     for (int d = 0; d < ND; ++d) oacc[d] = f32x4_t{};
     float m_run = kNegInf, l_run = 0.f;
 
-    // KV pipeline over the item's steps (stage j & 1 holds step j). V(i+1) is issued at the
-    // start of iteration i, K(i+2) right after S^T(i) has been read out of its stage, so each
-    // DMA has about one and a half iterations to land. Every iteration issues exactly one K
-    // and one V transfer (empty past the end), which keeps the vmcnt bookkeeping uniform.
-    constexpr int kDmaOps = T::kLoads;  // vector-memory operations per K or V transfer
-    const int n = w.c_end - w.c_begin;
-    Step cur = describe_step<D, kDense>(p, w, kv, w.c_begin);
-    Step nxt = n > 1 ? describe_step<D, kDense>(p, w, kv, w.c_begin + 1) : empty_step();
-    issue_step<E, D, kDense, true, true>(p, w, kv, cur, lk0, lv0);
-    issue_step<E, D, kDense, true, false>(p, w, kv, nxt, lk1, nullptr);
-    wait_vm<0>();
-    __syncthreads();
-
-    auto run_step = [&](auto stage_c, int i) {
-      constexpr int stg = decltype(stage_c)::value;
-      const char* lk = stg ? lk1 : lk0;
-      const char* lv = stg ? lv1 : lv0;
-      issue_step<E, D, kDense, false, true>(p, w, kv, nxt, nullptr, stg ? lv0 : lv1);
-      // S^T for keys 16*wave .. 16*wave+15.
-      f32x4_t s = f32x4_t{};
+    // Every sub-step issues kL K loads then kL V DMAs, so the counts below are exact: when
+    // sub-step s is computed, K(s) has 2*kL*kDecAhead + kL transfers issued after it and V(s)
+    // has 2*kL*kDecAhead.
+    const int n_sub = 4 * (w.c_end - w.c_begin);
+    u32x4_t kr[kStages][kL];
+    auto issue = [&](int s, u32x4_t (&kdst)[kL], char* vdst) {
+      const Sub u = s < n_sub ? describe_sub<D, kDense>(p, w, src, s) : Sub{0, 0, 0, 0};
+      // Rows outside [vlo, vhi) read past the buffer's end and so as zeros (one compare and
+      // one select per transfer; no branch, so the transfer count never varies).
+      const __amdgpu_buffer_rsrc_t rk = T::rsrc(static_cast<const S*>(p.k) + u.off);
+      const __amdgpu_buffer_rsrc_t rv = T::rsrc(static_cast<const S*>(p.v) + u.off);
+      // (The offsets stay below 2^31; setting bit 31 moves them out of range. Written as an OR
+      // rather than a select, which the compiler may turn into two predicated loads.)
+      const uint32_t nv = uint32_t(u.vhi - u.vlo);
+      const uint32_t kout = uint32_t(uint32_t(lc - u.vlo) >= nv) << 31;
 #pragma unroll
-      for (int c = 0; c < NQK; ++c) {
-        using F = typename E::Frag;
-        s = mma16(lds_ld<F>(lk + kaddr[c]), qf[c], s);
+      for (int j = 0; j < kL; ++j)
+        kdst[j] = buffer_ld16(rk, (k_lane + 64u * j) | kout);
+#pragma unroll
+      for (int j = 0; j < kL; ++j) {
+        const int row = (64 * j + lane) / T::kChunks;
+        const uint32_t vout = uint32_t(uint32_t(row - u.vlo) >= nv) << 31;
+        buffer_dma16(rv, vdst + 1024 * j, v_lane[j] | vout);
       }
-      kv_barrier<2 * kDmaOps>();
-      const Step nn = i + 2 < n ? describe_step<D, kDense>(p, w, kv, w.c_begin + i + 2) : empty_step();
-      issue_step<E, D, kDense, true, false>(p, w, kv, nn, stg ? lk1 : lk0, nullptr);
+    };
+#pragma unroll
+    for (int s = 0; s < kDecAhead; ++s) issue(s, kr[s], ring(s));
 
-      const bool full = cur.vlo == 0 && cur.vhi == kChunk;
-      const int last = cur.pos0 + kChunk - 1;
+    auto run_sub = [&](auto stage_c, int s) {
+      constexpr int stg = decltype(stage_c)::value;  // s % kStages
+      constexpr int nxt = (stg + kDecAhead) % kStages;
+      issue(s + kDecAhead, kr[nxt], ring(nxt));
+      const Sub u = describe_sub<D, kDense>(p, w, src, s);
+      wait_vm<2 * kL * kDecAhead + kL>();
+      // S^T[key][row] for the sub-step's 16 keys: lane holds keys 4*k4 .. 4*k4+3 of row lc.
+      f32x4_t sc = f32x4_t{};
+#pragma unroll
+      for (int j = 0; j < kL; ++j) {
+        if constexpr (kBf16) {
+          sc = mma16(__builtin_bit_cast(bf16x8_t, kr[stg][j]), qf[j], sc);
+        } else {
+          const f32x4_t kf = __builtin_bit_cast(f32x4_t, kr[stg][j]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc = mma16(kf[e], qf[4 * j + e], sc);
+        }
+      }
+      const bool full = u.vlo == 0 && u.vhi == kSub;
+      const int last = u.pos0 + kSub - 1;
       const bool clear = full && last <= pmin &&
-                         (kind == SP_GLOBAL || last < sink || cur.pos0 > pmax - window);
+                         (kind == SP_GLOBAL || last < sink || u.pos0 > pmax - window);
       if (kDense || !clear) {
-        const bool dual = step_is_dual(cur, kind, sink, window, pmin);
-        const KeyMask km = key_mask(cur, p_row, kind, sink, window, dual, 4 * k4);
+        const Step st{0, 0, u.vlo, u.vhi, u.pos0, 0};
+        const KeyMask km = key_mask(st, p_row, kind, sink, window, true, 4 * k4);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) s[rr] = in_mask(km, 16 * wave + rr, dual) ? s[rr] : kNegInf;
+        for (int rr = 0; rr < 4; ++rr) sc[rr] = in_mask(km, rr, true) ? sc[rr] : kNegInf;
       }
-      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * p.scale_log2);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      float rs = 0.f;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        s[rr] = exp2_fast(__builtin_fmaf(s[rr], p.scale_log2, -m_use));
-        rs += s[rr];
-      }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      if (__ballot(alpha != 1.f) != 0) {
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
+      // Softmax reference with 2^kSlack headroom, as in the prefill kernel.
+      if (__ballot(mx > m_run + kSlack) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2_fast(m_run - (m_new == kNegInf ? 0.f : m_new));
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
         for (int d = 0; d < ND; ++d) oacc[d] *= alpha;
       }
-      // O^T[dim][row] += V^T P^T over this wave's 16 keys.
+      const float m_use = m_run == kNegInf ? 0.f : m_run;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) sc[rr] = exp2_fast(__builtin_fmaf(sc[rr], p.scale_log2, -m_use));
+      l_run += (sc[0] + sc[1]) + (sc[2] + sc[3]);
+      wait_vm<2 * kL * kDecAhead>();
+      const char* lv = ring(stg);
+      // O^T[dim][row] += V^T P^T over the sub-step's 16 keys.
       if constexpr (kBf16) {
         const s16x4_t b = __builtin_bit_cast(
-            s16x4_t, u32x2_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])});
+            s16x4_t, u32x2_t{pack_bf16x2(sc[0], sc[1]), pack_bf16x2(sc[2], sc[3])});
 #pragma unroll
-        for (int d = 0; d < ND; ++d) {
+        for (int d = 0; d < ND; ++d)
           oacc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_tr4(lv + vaddr[d]), b, oacc[d],
                                                               0, 0, 0);
-        }
       } else {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
 #pragma unroll
           for (int d = 0; d < ND; ++d) {
-            const float a = lds_ld<float>(lv + T::off(16 * wave + 4 * k4 + rr, 4 * (16 * d + lc)));
-            oacc[d] = mma16(a, s[rr], oacc[d]);
+            const float a = lds_ld<float>(lv + T::off(4 * k4 + rr, 4 * (16 * d + lc)));
+            oacc[d] = mma16(a, sc[rr], oacc[d]);
           }
         }
       }
-      kv_barrier<2 * kDmaOps>();
-      cur = nxt;
-      nxt = nn;
     };
-    for (int i = 0; i < n; i += 2) {
-      run_step(std::integral_constant<int, 0>{}, i);
-      if (i + 1 < n) run_step(std::integral_constant<int, 1>{}, i + 1);
+    static_assert(kStages == 4, "the sub-step loop below is unrolled for four stages");
+    for (int s = 0; s < n_sub; s += 4) {
+      run_sub(std::integral_constant<int, 0>{}, s);
+      run_sub(std::integral_constant<int, 1>{}, s + 1);
+      run_sub(std::integral_constant<int, 2>{}, s + 2);
+      run_sub(std::integral_constant<int, 3>{}, s + 3);
     }
-    // Every wave's trailing K transfers (zero fills past the last step) target the K stages
-    // that hold the merge scratch below: all of them must have landed before any wave writes
-    // there, so wait for this wave's own and then meet the others.
-    kv_barrier<0>();
+    // The trailing transfers (zero fills past the last sub-step) must land before the ring is
+    // written by the next item.
+    wait_vm<0>();
 
-    // Merge the four waves' partial softmax states through LDS.
-    float l_w = l_run + __shfl_xor(l_run, 16);
-    l_w += __shfl_xor(l_w, 32);
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        scratch(wave, lc)[16 * d + 4 * k4 + rr] = oacc[d][rr];
-    if (k4 == 0) {
-      s_ml[wave][lc][0] = m_run;
-      s_ml[wave][lc][1] = l_w;
-    }
-    __syncthreads();
-    for (int e = tid; e < kDecodeRows * D; e += 256) {
-      const int q = e / D, dim = e - q * D;
-      if (q >= rows) continue;
-      float M = kNegInf;
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_ml[ww][q][0]);
-      const float Mu = M == kNegInf ? 0.f : M;
-      float acc = 0.f, lsum = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        const float f = exp2_fast(s_ml[ww][q][0] - Mu);
-        acc += f * scratch(ww, q)[dim];
-        lsum += f * s_ml[ww][q][1];
-      }
-      const int tq = q / p.G, gq = q - tq * p.G;
+    // Epilogue: lane holds dims 16d + 4*k4 + r of query row lc.
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (row_ok) {
+      const int q = lc;
       if (w.part < 0) {
-        const int64_t orw = int64_t(w.q_row0 + w.tq0 + tq) * p.Hq + int64_t(w.h) * p.G + gq;
-        const float val = lsum > 0.f ? acc / lsum : 0.f;
-        if constexpr (kBf16) {
-          obase[orw * D + dim] = uint16_t(pack_bf16x2(val, 0.f) & 0xffffu);
-        } else {
-          obase[orw * D + dim] = val;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        S* dst = obase + orow * D;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const int dim = 16 * d + 4 * k4;
+          if constexpr (kBf16) {
+            *reinterpret_cast<u32x2_t*>(dst + dim) =
+                u32x2_t{pack_bf16x2(oacc[d][0] * inv, oacc[d][1] * inv),
+                        pack_bf16x2(oacc[d][2] * inv, oacc[d][3] * inv)};
+          } else {
+            *reinterpret_cast<f32x4_t*>(dst + dim) = oacc[d] * inv;
+          }
         }
       } else {
-        part_o[(int64_t(w.part) * kDecodeRows + q) * D + dim] = acc;
-        if (dim == 0) {
-          part_ml[(int64_t(w.part) * kDecodeRows + q) * 2 + 0] = M;
-          part_ml[(int64_t(w.part) * kDecodeRows + q) * 2 + 1] = lsum;
+        float* po = part_o + (int64_t(w.part) * kDecodeRows + q) * D;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+          *reinterpret_cast<f32x4_t*>(po + 16 * d + 4 * k4) = oacc[d];
+        if (k4 == 0) {
+          part_ml[(int64_t(w.part) * kDecodeRows + q) * 2 + 0] = m_run;
+          part_ml[(int64_t(w.part) * kDecodeRows + q) * 2 + 1] = l_tot;
         }
       }
     }
-    __syncthreads();
   }
-  if (tid == 0) retire(p.ws, kOffDecodeCnt, kOffDecodeDone);
+  if (lane == 0) retire(p.ws, kOffDecodeCnt, kOffDecodeDone);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1107,7 +1205,7 @@ int occ_of(bool decode) {
   int n = 0;
   hipError_t e;
   if (decode)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<E, D, MODE>, 256, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<E, D, MODE>, 64, 0);
   else
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_kernel<E, D, MODE>, 256, 0);
   if (e != hipSuccess || n < 1) n = 1;
@@ -1117,7 +1215,7 @@ int occ_of(bool decode) {
 template <class E, int D, int MODE>
 hipError_t launch_attn_t(bool decode, int grid, const AttnParams& p, hipStream_t st) {
   if (decode)
-    decode_kernel<E, D, MODE><<<grid, 256, 0, st>>>(p);
+    decode_kernel<E, D, MODE><<<grid, 64, 0, st>>>(p);
   else
     prefill_kernel<E, D, MODE><<<grid, 256, 0, st>>>(p);
   return hipGetLastError();
