@@ -1095,57 +1095,93 @@ __global__ void __launch_bounds__(64) decode_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Combine: merges the partials of each KV-split block in split order.
+// Combine: merges the partials of each KV-split block. A work group is 16 lanes x D/8
+// dimension groups and takes one of 8 units of a block. Blocks with at most 8 splits or
+// more than 16 rows (prefill): unit k merges rows 16k .. 16k+15, a lane per row. Blocks of
+// up to 16 rows with more splits (decode): unit k merges rows 2k and 2k+1, 8 split lanes per
+// row; split lane j folds splits j, j + 8, ... and the lanes are then folded in lane order.
+// Every fold is an online rescale whose loads do not wait on earlier results, and the order
+// is fixed, so O is bitwise reproducible.
 // ---------------------------------------------------------------------------------------
+struct MergeState {
+  float m, l;
+  f32x4_t a0, a1;
+};
+
+__device__ __forceinline__ void merge_into(MergeState& s, float m, float l, f32x4_t o0,
+                                           f32x4_t o1) {
+  const float mn = fmaxf(s.m, m);
+  const float mu = mn == kNegInf ? 0.f : mn;
+  const float fa = exp2_fast(s.m - mu), fb = exp2_fast(m - mu);
+  s.l = s.l * fa + l * fb;
+  s.a0 = s.a0 * fa + o0 * fb;
+  s.a1 = s.a1 * fa + o1 * fb;
+  s.m = mn;
+}
+
 template <class E, int D>
 __global__ void __launch_bounds__(256) combine_kernel(AttnParams p) {
   using S = typename E::S;
-  constexpr int kTpr = D / 8;                  // threads per row, 8 dims each
-  constexpr int kRowsPerUnit = 256 / kTpr;     // rows merged by one work group pass
-  constexpr int kUnitsPerItem = kTileRows / kRowsPerUnit;
+  constexpr int kTpr = D / 8;                 // dimension groups of 8
+  constexpr int kLanes = 16;                  // lanes (threads past 16 * kTpr idle)
+  constexpr int kUnits = kTileRows / kLanes;  // 8 units per block
+  static_assert(kLanes * kTpr <= 256, "a unit fits the work group");
+  __shared__ MergeState s_state[kLanes][kTpr];
   if (!header_ok(p)) return;
   const WsHeader* hd = reinterpret_cast<const WsHeader*>(p.ws);
   const CombineItem* items = reinterpret_cast<const CombineItem*>(p.ws + hd->off_combine);
   S* obase = static_cast<S*>(p.o);
-  const int n_units = hd->n_combine * kUnitsPerItem;
-  const int lr = threadIdx.x / kTpr, d0 = (threadIdx.x % kTpr) * 8;
+  const int n_units = hd->n_combine * kUnits;
+  const bool act = threadIdx.x < kLanes * kTpr;
+  const int ln = act ? threadIdx.x / kTpr : 0, dg = threadIdx.x % kTpr, d0 = dg * 8;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
-    const CombineItem c = items[u / kUnitsPerItem];
-    const int r = (u % kUnitsPerItem) * kRowsPerUnit + lr;
+    const CombineItem c = items[u / kUnits];
+    const int k = u % kUnits;
     const int rows = c.nq * p.G;
-    if (r >= rows) continue;
+    const bool by_split = rows <= kDecodeRows && c.nsplit > kUnits;  // uniform per unit
+    const int r = by_split ? 2 * k + (ln >> 3) : kLanes * k + ln;
+    const int j0 = by_split ? (ln & 7) : 0, js = by_split ? 8 : 1;
     const int rows_max = c.kind == 0 ? kTileRows : kDecodeRows;
     const float* po = reinterpret_cast<const float*>(p.ws + (c.kind == 0 ? hd->off_part_pre
                                                                         : hd->off_part_dec));
     const float* pm = reinterpret_cast<const float*>(p.ws + (c.kind == 0 ? hd->off_ml_pre
                                                                         : hd->off_ml_dec));
-    float M = kNegInf;
-    for (int s = 0; s < c.nsplit; ++s)
-      M = fmaxf(M, pm[(int64_t(c.part0 + s) * rows_max + r) * 2]);
-    const float Mu = M == kNegInf ? 0.f : M;
-    f32x4_t a0 = f32x4_t{}, a1 = f32x4_t{};
-    float lsum = 0.f;
-    for (int s = 0; s < c.nsplit; ++s) {
-      const int64_t slot = int64_t(c.part0 + s) * rows_max + r;
-      const float f = exp2_fast(pm[slot * 2] - Mu);
-      lsum += f * pm[slot * 2 + 1];
-      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(po + slot * D + d0);
-      a0 += f * src[0];
-      a1 += f * src[1];
+    MergeState st{kNegInf, 0.f, f32x4_t{}, f32x4_t{}};
+    if (act && r < rows) {
+#pragma unroll 8
+      for (int s = j0; s < c.nsplit; s += js) {
+        const int64_t slot = int64_t(c.part0 + s) * rows_max + r;
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(po + slot * D + d0);
+        merge_into(st, pm[slot * 2], pm[slot * 2 + 1], src[0], src[1]);
+      }
     }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    a0 *= inv;
-    a1 *= inv;
-    const int tq = r / p.G, g = r - tq * p.G;
-    const int64_t orow = int64_t(c.q_row0 + c.tq0 + tq) * p.Hq + int64_t(c.h) * p.G + g;
-    if constexpr (sizeof(S) == 2) {
-      u32x4_t v = {pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]),
-                   pack_bf16x2(a1[0], a1[1]), pack_bf16x2(a1[2], a1[3])};
-      *reinterpret_cast<u32x4_t*>(obase + orow * D + d0) = v;
-    } else {
-      f32x4_t* dst = reinterpret_cast<f32x4_t*>(obase + orow * D + d0);
-      dst[0] = a0;
-      dst[1] = a1;
+    bool write = act && r < rows;
+    if (by_split) {
+      if (act) s_state[ln][dg] = st;
+      __syncthreads();
+      write = write && (ln & 7) == 0;
+      if (write) {
+        for (int j = 1; j < 8 && j < c.nsplit; ++j) {
+          const MergeState& o = s_state[ln + j][dg];
+          merge_into(st, o.m, o.l, o.a0, o.a1);
+        }
+      }
+      __syncthreads();
+    }
+    if (write) {
+      const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+      const f32x4_t a0 = st.a0 * inv, a1 = st.a1 * inv;
+      const int tq = r / p.G, g = r - tq * p.G;
+      const int64_t orow = int64_t(c.q_row0 + c.tq0 + tq) * p.Hq + int64_t(c.h) * p.G + g;
+      if constexpr (sizeof(S) == 2) {
+        u32x4_t v = {pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]),
+                     pack_bf16x2(a1[0], a1[1]), pack_bf16x2(a1[2], a1[3])};
+        *reinterpret_cast<u32x4_t*>(obase + orow * D + d0) = v;
+      } else {
+        f32x4_t* dst = reinterpret_cast<f32x4_t*>(obase + orow * D + d0);
+        dst[0] = a0;
+        dst[1] = a1;
+      }
     }
   }
 }
