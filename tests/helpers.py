@@ -74,3 +74,21 @@ def assert_parity(got: np.ndarray, ref: np.ndarray, case, label=""):
     print("%s %s: maxabs=%.3e min_cos=%.8f" % (case.name, label, maxabs, cos), flush=True)
     assert maxabs <= MAXABS[case.dtype], (label, maxabs)
     assert cos > COS_MIN, (label, cos)
+
+
+def sample_rows(case, budget_rows: int, seed: int = 4321):
+    """Seeded sample of (request, query head, token indices) for full-size checks."""
+    rng = np.random.default_rng(seed)
+    picks = [(b, hq, int(case.q_len[b])) for b in range(case.B) if case.q_len[b] > 0
+             for hq in range(case.Hq)]
+    order = rng.permutation(len(picks))
+    per = max(1, budget_rows // max(1, len(picks)))
+    out, rows = [], 0
+    for i in order:
+        if rows >= budget_rows:
+            break
+        b, hq, nq = picks[i]
+        toks = np.arange(nq) if nq <= per else np.sort(rng.choice(nq, per, replace=False))
+        out.append((b, hq, toks))
+        rows += len(toks)
+    return out

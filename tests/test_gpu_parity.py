@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import oracle
-from tests.helpers import (DEV, assert_parity, run_dense_mask, run_segpaged, to_device, to_f64)
+from tests.helpers import (COS_MIN, DEV, MAXABS, assert_parity, run_dense_mask, run_segpaged,
+                           sample_rows, to_device, to_f64)
 from workloads import GLOBAL, LOCAL, config_case, custom_case, free_list
 
 pytestmark = pytest.mark.gpu
@@ -173,3 +174,40 @@ def test_decode_repeat_is_bitwise_identical():
         torch.cuda.synchronize()
         assert torch.equal(out, o2)
     assert layer.check() == 0
+
+
+@pytest.mark.parametrize("index,budget", [(2, 48), (3, 24), (4, 24)])
+def test_full_size_workload_sampled_rows(index, budget):
+    # The full workloads, planned for this device exactly as the benchmark runs them: page
+    # tables bit-exact, two heads' pool pages bit-exact, and seeded sampled output rows against
+    # the oracle (the whole output is too large for the fp64 oracle).
+    c = config_case(index)
+    print("case full-size", c.name, flush=True)
+    out, layer = run_segpaged(c)
+    seg_o, kvl_o, n_virt = oracle.plan_tables(c.ctx_len, c.q_len, c.policy, c.P)
+    np.testing.assert_array_equal(layer.seg_table.cpu().numpy(), seg_o)
+    np.testing.assert_array_equal(layer.kv_len.cpu().numpy(), kvl_o)
+    assert layer.n_virt == n_virt
+    fl = free_list(c.seed, n_virt)
+    rng = np.random.default_rng(index)
+    for _ in range(2):
+        b, h = int(rng.integers(c.B)), int(rng.integers(c.Hkv))
+        pos, page, slot = (np.array(x) for x in zip(*oracle.gather_positions(seg_o, fl, c.P, b, h)))
+        base = int(np.sum(c.ctx_len[:b]))
+        kp = layer.k_pool[torch.from_numpy(page).long().to(DEV), torch.from_numpy(slot).long().to(DEV)]
+        vp = layer.v_pool[torch.from_numpy(page).long().to(DEV), torch.from_numpy(slot).long().to(DEV)]
+        np.testing.assert_array_equal(kp.cpu().view(torch.int16).numpy(), c.k[base + pos, h].view(np.int16))
+        np.testing.assert_array_equal(vp.cpu().view(torch.int16).numpy(), c.v[base + pos, h].view(np.int16))
+    got = to_f64(out)
+    q_row0 = np.concatenate([[0], np.cumsum(c.q_len)[:-1]])
+    worst_abs, worst_cos = 0.0, 1.0
+    for b, hq, toks in sample_rows(c, budget):
+        ref = oracle.attention_rows(c.q, c.k, c.v, c.ctx_len, c.q_len, c.policy, c.Hq, c.Hkv,
+                                    c.scale, c.dtype, b, hq, toks)
+        g = got[q_row0[b] + toks, hq, :]
+        worst_abs = max(worst_abs, float(np.abs(g - ref).max()))
+        cos = float(g.ravel() @ ref.ravel() / (np.linalg.norm(g) * np.linalg.norm(ref)))
+        worst_cos = min(worst_cos, cos)
+    print("%s sampled: maxabs=%.3e min_cos=%.8f" % (c.name, worst_abs, worst_cos), flush=True)
+    assert worst_abs <= MAXABS[c.dtype]
+    assert worst_cos > COS_MIN
