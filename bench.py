@@ -130,7 +130,16 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="rows of the CPU-oracle sample (default sized for about 10-30 s)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense+mask timing")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the run, copy MIB MiB device-to-device 3 times (a plain copy "
+                         "kernel of known size for calibrating rocprofv3 byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: turn two rocprofv3 --pmc runs of this workload "
+                         "(FETCH_SIZE, then WRITE_SIZE, each with --copy-calibration) into "
+                         "HBM bytes per launch of its main kernel in profiles/traffic.json")
     args = ap.parse_args()
+    if args.traffic_from:
+        return write_traffic(args)
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -292,6 +301,70 @@ def main() -> int:
                                                            case.B * case.Hq, cpu_s)},
     }
     print(json.dumps(line), flush=True)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    return 0
+
+
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _counter_rows(d: str, counter: str):
+    """(kernel name, value) per dispatch of one rocprofv3 --pmc csv run directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under " + d)
+    out = []
+    for r in csv.DictReader(open(files[0])):
+        if r["Counter_Name"] == counter:
+            out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def write_traffic(args) -> int:
+    """HBM bytes per launch of the workload's main kernel from FETCH_SIZE / WRITE_SIZE runs.
+
+    Both counters are in KiB per dispatch. Each is scaled by the factor that makes it read
+    right for the largest device-to-device copy in the same run (copy_bytes read and written).
+    """
+    from workloads import config_case
+    case = config_case(args.config, with_tensors=False)
+    decode = bool((case.q_len * (case.Hq // case.Hkv) <= 16).all())
+    kernel = "decode_kernel" if decode else "prefill_kernel"
+    copy_bytes = float(args.copy_calibration << 20)
+    if copy_bytes <= 0:
+        raise SystemExit("--traffic-from needs --copy-calibration MIB of the counter runs")
+    rec = {"kernel": kernel, "copy_bytes": copy_bytes}
+    for d, counter in zip(args.traffic_from, ("FETCH_SIZE", "WRITE_SIZE")):
+        rows = _counter_rows(d, counter)
+        main = [v for n, v in rows if kernel + "<" in n and ", 0>" in n]
+        copy = [v for n, v in rows if COPY_KERNEL in n]
+        if not main or not copy:
+            raise SystemExit("%s: main or copy kernel missing in %s" % (counter, d))
+        per = float(np.mean(main))
+        cal = max(copy)
+        factor = copy_bytes / (cal * 1024.0)
+        key = "fetch" if counter == "FETCH_SIZE" else "write"
+        rec[key + "_kib_per_launch"] = round(per, 1)
+        rec[key + "_copy_kib"] = round(cal, 1)
+        rec[key + "_factor"] = round(factor, 4)
+        rec[key + "_bytes"] = per * 1024.0 * factor
+    rec["bytes_per_launch"] = round(rec.pop("fetch_bytes") + rec.pop("write_bytes"))
+    rec["source_hash"] = source_hash()
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data.setdefault(case.name, {})[kernel] = rec
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({case.name: rec}))
     return 0
 
 
