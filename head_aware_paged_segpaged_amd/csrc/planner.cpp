@@ -342,7 +342,7 @@ sp_status make_plan(const Shape& s, int32_t slots_prefill, int32_t slots_decode,
   std::vector<Tile> pre_items, dec_items;
   std::vector<CombineItem> combine;
   int32_t n_part_pre = 0, n_part_dec = 0;
-  split_tiles(pre_tiles, slots_prefill, /*min_split=*/16, 0, &pre_items, &combine, &n_part_pre);
+  split_tiles(pre_tiles, slots_prefill, /*min_split=*/8, 0, &pre_items, &combine, &n_part_pre);
   split_tiles(dec_tiles, slots_decode, /*min_split=*/32, 1, &dec_items, &combine, &n_part_dec);
 
   WsHeader& hd = out->hdr;
