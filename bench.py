@@ -55,12 +55,18 @@ def stored_rows(case, kv_len) -> float:
 
 
 def source_hash() -> str:
+    """Hash of the library sources with comments and blank space removed (a kernel change,
+    not a comment edit, invalidates stored counter results)."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "head_aware_paged_segpaged_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(name.encode())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -141,7 +147,7 @@ def main() -> int:
     if args.traffic_from:
         return write_traffic(args)
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
 

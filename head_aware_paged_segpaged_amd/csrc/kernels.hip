@@ -7,18 +7,18 @@
 // batch run in one persistent launch that pops work items from per-XCD queues.
 //
 // Data layout in the kernels:
-// - One KV step = 64 stored tokens of one segment (64-aligned in the segment), staged in LDS
-//   as K [64][D + pad] (row-major) and V^T [D][64 + pad] (transposed while storing, so that
-//   the P*V contraction reads 8 consecutive keys per lane), double-buffered, with the next
-//   step's global loads in flight in registers while the current step is computed.
-// - Prefill tile: 128 rows = (query token, query head of the GQA group) pairs of one KV
-//   head; wave w owns rows 32w..32w+31. S^T = K * Q^T on 32x32 MFMA puts one query row per
-//   lane column, so the softmax row statistics are per lane (plus one cross-half exchange)
-//   and the O^T accumulators are rescaled in-lane.
-// - Decode item: up to 16 rows; wave w takes keys 16w..16w+15 of each step on 16x16 MFMA and
-//   keeps its own running (m, l, O); the four waves merge through LDS at the end.
-// Softmax runs in base 2 with scale*log2(e) folded into one FMA; masks are evaluated only on
-// steps that straddle a visibility edge or are not full.
+// - Prefill: one KV step = 64 stored tokens of one segment (64-aligned in the segment). K and V
+//   of a step arrive by LDS-DMA into row-major LDS tiles whose 16-byte chunks are XOR-swizzled
+//   by row (conflict-free fragment and transposed reads); two K and two V stages. A tile is
+//   128 rows = (query token, query head of the GQA group) pairs of one KV head; wave w owns
+//   rows 32w..32w+31. S^T = K * Q^T on 32x32 MFMA puts one query row per lane column, so the
+//   softmax row statistics are per lane (plus one cross-half exchange) and the O^T
+//   accumulators are rescaled in-lane; V^T comes from the LDS transpose reads.
+// - Decode: one wave per item of up to 16 rows, in sub-steps of 16 keys: K straight into
+//   registers, V into a wave-private LDS ring, three sub-steps ahead, no work-group barrier.
+// Softmax runs in base 2 with scale*log2(e) folded into one FMA, against a per-row reference
+// that moves only when a row maximum passes it by more than 2^kSlack; masks are evaluated only
+// on steps that straddle a visibility edge or are not full.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
