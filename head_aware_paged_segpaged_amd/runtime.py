@@ -50,6 +50,12 @@ class SegPagedLayer:
                                      device=self.device)
         self.kv_len = torch.zeros((max(Bn, 1), self.Hkv), dtype=torch.int32, device=self.device)
         self.v2p = torch.zeros((max(self.n_virt, 1),), dtype=torch.int32, device=self.device)
+        self.rebuild(k_dense, v_dense, fl, stream)
+
+    def rebuild(self, k_dense: torch.Tensor, v_dense: torch.Tensor, free_pages,
+                stream=None) -> None:
+        """Refill the already allocated pool and tables (no allocation)."""
+        fl = np.asarray(free_pages, dtype=np.int32)
         B.segpaged_build(self.dtype, self.D, self.P, self.ctx_len, self.q_len, self.policy,
                          k_dense, v_dense, fl, self.n_phys, self.k_pool, self.v_pool,
                          self.seg_table, self.kv_len, self.v2p, stream)

@@ -87,6 +87,10 @@ CONFIGS = [
     dict(name="mha64_128k_prefill4096", dtype="bf16", Hq=64, Hkv=64, D=128, P=64, B=1,
          L=("fixed", [131072]), q=("fixed", 4096), globals=("fixed", list(range(0, 64, 8))),
          sink=4, window=128, q_std=1.0 / math.sqrt(128), kv_std=1.0),
+    # The long-context slice of the decode workload: every request at 32K-128K.
+    dict(name="qwen3_32b_decode_b64_32k_128k", dtype="bf16", Hq=64, Hkv=8, D=128, P=64, B=64,
+         L=("log_uniform", 32768, 131072), q=("fixed", 1), globals=("draw", 2),
+         sink=4, window=512, q_std=1.0 / math.sqrt(128), kv_std=1.0),
 ]
 
 
