@@ -143,9 +143,14 @@ def main() -> int:
                     help="no GPU run: turn two rocprofv3 --pmc runs of this workload "
                          "(FETCH_SIZE, then WRITE_SIZE, each with --copy-calibration) into "
                          "HBM bytes per launch of its main kernel in profiles/traffic.json")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="only time torch's bf16 GEMM (hipBLASLt) at 4096^3..16384^3: what a "
+                         "vendor-tuned dense contraction reaches on this GPU, for context")
     args = ap.parse_args()
     if args.traffic_from:
         return write_traffic(args)
+    if args.gemm_reference:
+        return gemm_reference()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -321,6 +326,27 @@ def main() -> int:
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+    return 0
+
+
+def gemm_reference() -> int:
+    """TFLOP/s of torch.matmul on square bf16 matrices (the vendor GEMM library)."""
+    import torch
+    out = {}
+    for n in (4096, 8192, 16384):
+        a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+        b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+        for _ in range(3):
+            a @ b
+        torch.cuda.synchronize()
+        iters = 20 if n < 16384 else 5
+        t0 = time.perf_counter()
+        for _ in range(iters):
+            a @ b
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / iters
+        out[str(n)] = round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+    print(json.dumps({"bf16_gemm_tflops": out, "peak": PEAK_BF16_TFLOPS}), flush=True)
     return 0
 
 
