@@ -105,6 +105,11 @@ sp_status run_attention(const Shape& s, const void* q, const void* k, const void
       (seg_table == nullptr || kv_len == nullptr || v2p == nullptr || n_phys < 1))
     return SP_ERR_INVALID_ARG;
   if (ws_bytes < size_t(kHeaderBytes)) return SP_ERR_WORKSPACE_TOO_SMALL;
+  // Prefill with pages smaller than a KV step addresses rows from the pool start with 32-bit
+  // byte offsets.
+  if (need_pre && s.mode == kModePaged && s.P < kChunk &&
+      n_phys * int64_t(s.P) * s.D * (s.dtype == SP_BF16 ? 2 : 4) > int64_t(0x7fffffff))
+    return SP_ERR_UNSUPPORTED;
   int32_t gp = 0, gd = 0;
   st = grids(s, &gp, &gd);
   if (st != SP_OK) return st;

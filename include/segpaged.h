@@ -156,7 +156,10 @@ sp_status segpaged_attention_plan(sp_dtype dtype, int32_t B, int32_t Hq, int32_t
  * prefill kernel; KV-split items are merged by a fixed-order combine kernel, so O is bitwise
  * reproducible. Calls that share one workspace must not overlap in time.
  * Errors: SP_ERR_PLAN_MISMATCH if the workspace was planned for other arguments (checked on
- * the device; the kernels then write nothing -- see segpaged_attention_check). */
+ * the device; the kernels then write nothing -- see segpaged_attention_check);
+ * SP_ERR_UNSUPPORTED if page_size < 64, some request takes the prefill kernel and a pool is
+ * larger than 2 GiB (that path addresses pool rows with 32-bit offsets). O is unspecified when
+ * the device-side error word reports SP_ERR_INVALID_ARG (a page id >= n_phys in v2p). */
 sp_status segpaged_attention(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                              int32_t page_size, const int32_t* ctx_len, const int32_t* q_len,
                              const sp_head_policy* pol, const void* q, const void* k_pool,

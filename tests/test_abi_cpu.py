@@ -96,6 +96,18 @@ def test_invalid_arguments_are_rejected_on_the_host():
             == E.SP_ERR_INVALID_ARG)
 
 
+def test_small_page_prefill_pool_limit_is_checked_on_the_host():
+    # pages of 16 tokens, a prefill request, and a pool of 2^20 pages x 16 x 128 x 2 B = 4 GiB:
+    # rejected before any device call (the pointers are never dereferenced)
+    fake = binding.ctypes.c_void_p(0x10000)
+    c, q = np.array([1000], np.int32), np.array([100], np.int32)
+    pol = np.array([(0, 0, 1)], np.int32)
+    code = binding.lib().segpaged_attention(
+        0, 1, 8, 1, 128, 16, binding._ptr(c), binding._ptr(q), binding._ptr(pol), fake, fake,
+        fake, 1 << 20, fake, fake, fake, binding.ctypes.c_float(0.1), fake, fake, 1 << 20, None)
+    assert code == binding.SP_ERR_UNSUPPORTED
+
+
 def test_build_validates_free_list_before_touching_memory():
     ctx, q, pol = np.array([100], np.int32), np.array([10], np.int32), [(0, 0, 1)]
     n_virt = sp.segpaged_plan_pages(ctx, q, pol, 16)
