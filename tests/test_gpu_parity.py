@@ -211,3 +211,41 @@ def test_full_size_workload_sampled_rows(index, budget):
     print("%s sampled: maxabs=%.3e min_cos=%.8f" % (c.name, worst_abs, worst_cos), flush=True)
     assert worst_abs <= MAXABS[c.dtype]
     assert worst_cos > COS_MIN
+
+
+def _random_cases(n=16, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = "f32" if i % 5 == 4 else "bf16"
+        D = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 3]))
+        G = int(rng.choice([1, 2, 4, 6, 8, 16]))
+        P = int(rng.choice([16, 32, 64, 128, 256]))
+        B = int(rng.integers(1, 4))
+        ctx = rng.integers(1, 1500, B)
+        q = np.minimum(ctx, rng.choice([1, 1, 2, 5, 40, 200], B))
+        pol = []
+        for _ in range(Hkv):
+            if rng.random() < 0.35:
+                pol.append((G_, 0, 1))
+            else:
+                pol.append((L_, int(rng.choice([0, 1, 4, 100])), int(rng.choice([1, 17, 64, 300]))))
+        out.append(dict(seed=500 + i, dtype=dtype, Hq=Hkv * G, Hkv=Hkv, D=D, P=P,
+                        ctx_len=list(ctx), q_len=list(q), policy=pol))
+    return out
+
+
+@pytest.mark.parametrize("args", _random_cases(), ids=lambda a: "seed%d" % a["seed"])
+def test_random_shapes_against_oracle(args):
+    # Seeded random shapes across dtypes, head dims, GQA groups, page sizes, request mixes
+    # (decode and prefill together) and policies.
+    a = dict(args)
+    c = custom_case(a.pop("seed"), **a)
+    print("case random", c.dtype, c.Hq, c.Hkv, c.D, c.P, list(c.ctx_len), list(c.q_len),
+          c.policy.tolist(), flush=True)
+    out, layer = run_segpaged(c)
+    seg_o, kvl_o, _ = oracle.plan_tables(c.ctx_len, c.q_len, c.policy, c.P)
+    np.testing.assert_array_equal(layer.seg_table.cpu().numpy()[:c.B], seg_o)
+    np.testing.assert_array_equal(layer.kv_len.cpu().numpy()[:c.B], kvl_o)
+    assert_parity(to_f64(out), _oracle(c), c, "random")
