@@ -1189,7 +1189,7 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnParams p) {
 // ---------------------------------------------------------------------------------------
 // Build / scatter: one work group copies 64 stored tokens (K and V) of one segment from the
 // dense [T][Hkv][D] tensors into their pool pages. Reads are whole D-rows, writes are whole
-// contiguous page rows.
+// contiguous page rows; both are streaming (non-temporal) accesses, each byte is touched once.
 // ---------------------------------------------------------------------------------------
 template <class E, int D>
 __global__ void __launch_bounds__(256) build_kernel(BuildParams p) {
@@ -1221,8 +1221,8 @@ __global__ void __launch_bounds__(256) build_kernel(BuildParams p) {
     kr[j] = vr[j] = u32x4_t{0u, 0u, 0u, 0u};
     if (ti < sg.ntok) {
       const int64_t src = (int64_t(sg.src_row0 + ti) * p.Hkv + sg.h) * D + col * kVec;
-      kr[j] = *reinterpret_cast<const u32x4_t*>(kd + src);
-      vr[j] = *reinterpret_cast<const u32x4_t*>(vd + src);
+      kr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kd + src));
+      vr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vd + src));
       const int phys = p.v2p[sg.vstart + ti / p.P];
       dst[j] = (int64_t(phys) * p.P + (ti & (p.P - 1))) * D + col * kVec;
     }
@@ -1230,8 +1230,8 @@ __global__ void __launch_bounds__(256) build_kernel(BuildParams p) {
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) {
     if (dst[j] >= 0) {
-      *reinterpret_cast<u32x4_t*>(kp + dst[j]) = kr[j];
-      *reinterpret_cast<u32x4_t*>(vp + dst[j]) = vr[j];
+      __builtin_nontemporal_store(kr[j], reinterpret_cast<u32x4_t*>(kp + dst[j]));
+      __builtin_nontemporal_store(vr[j], reinterpret_cast<u32x4_t*>(vp + dst[j]));
     }
   }
 }
