@@ -315,8 +315,9 @@ def main() -> int:
         "cpu_baseline": {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": threads,
                          "kind": "oracle",
                          "sample": "%d query rows (%d of %d (request, query head) pairs), "
-                                   "fp64 numpy, %.1f s" % (cpu_nrows, len(sample),
-                                                           case.B * case.Hq, cpu_s)},
+                                   "fp64 numpy (%s BLAS), %.1f s; host has %d CPUs"
+                                   % (cpu_nrows, len(sample), case.B * case.Hq, blas_name(),
+                                      cpu_s, os.cpu_count() or 0)},
     }
     print(json.dumps(line), flush=True)
     if args.copy_calibration > 0:
@@ -327,6 +328,13 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
     return 0
+
+
+def blas_name() -> str:
+    try:
+        return str(np.show_config(mode="dicts")["Build Dependencies"]["blas"]["name"])
+    except Exception:  # older numpy: no dict form
+        return "unknown"
 
 
 def gemm_reference() -> int:
