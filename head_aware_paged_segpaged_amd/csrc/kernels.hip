@@ -113,16 +113,30 @@ __device__ __forceinline__ void set_error(uint8_t* ws, int code) {
   atomicCAS(reinterpret_cast<int*>(ws + kOffError), 0, code);
 }
 
-// Pops the next work item: own XCD's queue first, then the others. Thread 0 only.
+// Work groups the round-robin dispatch places on XCD x (work group i runs on XCD i % kXcds).
+__device__ __forceinline__ int wgs_on_xcd(int x) {
+  return (int(gridDim.x) - x + kXcds - 1) / kXcds;
+}
+
+// Pops the next work item, one thread per work group. The first pop is static: the k-th work
+// group of an XCD takes item k of that XCD's queue, so the launch starts without a burst of
+// atomics on the queue counters. Later pops take the queue's counter (past the items handed
+// out statically): own XCD's queue first, then the others.
 __device__ __forceinline__ int pop_item(uint8_t* ws, const int32_t* qb, int cnt_off, int xcd,
-                                        uint32_t& exhausted) {
+                                        uint32_t& exhausted, bool& first) {
+  if (first) {
+    first = false;
+    const int k = int(blockIdx.x) / kXcds;
+    if (k < qb[xcd + 1] - qb[xcd]) return qb[xcd] + k;
+  }
   for (int k = 0; k < kXcds; ++k) {
     const int x = (xcd + k) & (kXcds - 1);
     if (exhausted & (1u << x)) continue;
     const int n = qb[x + 1] - qb[x];
-    if (n > 0) {
+    const int s = min(n, wgs_on_xcd(x));
+    if (n > s) {
       const int t = atomicAdd(reinterpret_cast<int*>(ws + cnt_off + x * 128), 1);
-      if (t < n) return qb[x] + t;
+      if (s + t < n) return qb[x] + s + t;
     }
     exhausted |= 1u << x;
   }
@@ -490,6 +504,7 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
   const int lq = lane & 31, hh = lane >> 5;
   const int xcd = blockIdx.x % kXcds;
   uint32_t exhausted = 0;
+  bool first = true;
   const S* qbase = static_cast<const S*>(p.q);
   S* obase = static_cast<S*>(p.o);
 
@@ -508,7 +523,7 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
   }
 
   for (;;) {
-    if (tid == 0) s_item = pop_item(p.ws, hd->prefill_q, kOffPrefillCnt, xcd, exhausted);
+    if (tid == 0) s_item = pop_item(p.ws, hd->prefill_q, kOffPrefillCnt, xcd, exhausted, first);
     __syncthreads();
     const int it = uniform(s_item);
     if (it < 0) break;
@@ -892,6 +907,7 @@ __global__ void __launch_bounds__(64) decode_kernel(AttnParams p) {
   const int lc = lane & 15, k4 = lane >> 4;
   const int xcd = blockIdx.x % kXcds;
   uint32_t exhausted = 0;
+  bool first = true;
   const S* qbase = static_cast<const S*>(p.q);
   S* obase = static_cast<S*>(p.o);
   const uint32_t rs = kDense ? uint32_t(p.Hkv) * T::kRowBytes : uint32_t(T::kRowBytes);
@@ -918,7 +934,7 @@ __global__ void __launch_bounds__(64) decode_kernel(AttnParams p) {
 
   for (;;) {
     int it = 0;
-    if (lane == 0) it = pop_item(p.ws, hd->decode_q, kOffDecodeCnt, xcd, exhausted);
+    if (lane == 0) it = pop_item(p.ws, hd->decode_q, kOffDecodeCnt, xcd, exhausted, first);
     it = uniform(it);
     if (it < 0) break;
     const WorkItem w = load_item(items, it);
