@@ -222,16 +222,28 @@ sp_status segpaged_build(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int3
       seen[size_t(f)] = 1;
     }
   }
-  std::vector<int32_t> tab(size_t(B) * Hkv * 8), kl(size_t(B) * Hkv);
-  layout_tables(lay, B, Hkv, tab.data(), kl.data());
-  if (hipMemcpyAsync(seg_table, tab.data(), tab.size() * 4, hipMemcpyHostToDevice, stream) !=
-          hipSuccess ||
-      hipMemcpyAsync(kv_len, kl.data(), kl.size() * 4, hipMemcpyHostToDevice, stream) !=
-          hipSuccess)
-    return SP_ERR_HIP;
-  if (n_virt > 0 && hipMemcpyAsync(v2p, free_pages, size_t(n_virt) * 4, hipMemcpyHostToDevice,
-                                   stream) != hipSuccess)
-    return SP_ERR_HIP;
+  // Tables: seg_table, kv_len and v2p. When the caller placed them back to back in one
+  // allocation they go up in a single host-to-device copy (each copy from pageable memory
+  // costs tens of microseconds of fixed overhead), else in three.
+  const size_t n_tab = size_t(B) * Hkv * 8, n_kl = size_t(B) * Hkv;
+  const bool adjacent = kv_len == seg_table + n_tab && (n_virt == 0 || v2p == kv_len + n_kl);
+  std::vector<int32_t> host(n_tab + n_kl + (adjacent ? size_t(n_virt) : 0));
+  layout_tables(lay, B, Hkv, host.data(), host.data() + n_tab);
+  if (adjacent) {
+    if (n_virt > 0) std::memcpy(host.data() + n_tab + n_kl, free_pages, size_t(n_virt) * 4);
+    if (hipMemcpyAsync(seg_table, host.data(), host.size() * 4, hipMemcpyHostToDevice,
+                       stream) != hipSuccess)
+      return SP_ERR_HIP;
+  } else {
+    if (hipMemcpyAsync(seg_table, host.data(), n_tab * 4, hipMemcpyHostToDevice, stream) !=
+            hipSuccess ||
+        hipMemcpyAsync(kv_len, host.data() + n_tab, n_kl * 4, hipMemcpyHostToDevice, stream) !=
+            hipSuccess)
+      return SP_ERR_HIP;
+    if (n_virt > 0 && hipMemcpyAsync(v2p, free_pages, size_t(n_virt) * 4,
+                                     hipMemcpyHostToDevice, stream) != hipSuccess)
+      return SP_ERR_HIP;
+  }
   if (hipStreamSynchronize(stream) != hipSuccess) return SP_ERR_HIP;
 
   // Scatter: one launch per run of at most kMaxBuildSegs non-empty segments.

@@ -865,12 +865,16 @@ __device__ __forceinline__ Sub describe_sub(const AttnParams& p, const WorkItem&
 }
 
 // 16 bytes per lane from a buffer into registers / into LDS at lds + 16 * lane (device-only
-// builtins kept out of the kernel body, which the host pass also parses).
+// builtins kept out of the kernel body, which the host pass also parses). Decode reads every
+// stored K/V byte exactly once, so these loads carry the non-temporal cache policy (NT, bit 1
+// of the buffer instruction's cache-policy operand): the stream neither allocates in nor
+// evicts from the L2s and the MALL, which lets it run closer to the HBM read rate.
+constexpr int kPolicyStream = 2;
 __device__ __forceinline__ u32x4_t buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kPolicyStream);
 }
 __device__ __forceinline__ void buffer_dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, off, 0, 0, kPolicyStream);
 }
 
 template <class E, int D, int MODE>
@@ -1222,33 +1226,31 @@ __global__ void __launch_bounds__(256) build_kernel(BuildParams p) {
   }
   const BuildSeg sg = p.seg[lo];
   const int ti0 = (c - sg.chunk0) * kChunk;
+  const int lp = __builtin_ctz(unsigned(p.P));  // page size: a power of two
   const S* kd = static_cast<const S*>(p.k);
   const S* vd = static_cast<const S*>(p.v);
   S* kp = static_cast<S*>(p.kp);
   S* vp = static_cast<S*>(p.vp);
+  // Every load is issued before any store, with no branch: lanes past the segment's end copy
+  // the segment's last token again (the same bytes to the same slot as the lane that owns it,
+  // in this work group), so all loads are unconditional and in flight at once.
   u32x4_t kr[kLoads], vr[kLoads];
   int64_t dst[kLoads];
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) {
     const int idx = threadIdx.x + 256 * j;
     const int row = idx / kCols, col = idx % kCols;
-    const int ti = ti0 + row;
-    dst[j] = -1;
-    kr[j] = vr[j] = u32x4_t{0u, 0u, 0u, 0u};
-    if (ti < sg.ntok) {
-      const int64_t src = (int64_t(sg.src_row0 + ti) * p.Hkv + sg.h) * D + col * kVec;
-      kr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kd + src));
-      vr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vd + src));
-      const int phys = p.v2p[sg.vstart + ti / p.P];
-      dst[j] = (int64_t(phys) * p.P + (ti & (p.P - 1))) * D + col * kVec;
-    }
+    const int ti = min(ti0 + row, sg.ntok - 1);
+    const int64_t src = (int64_t(sg.src_row0 + ti) * p.Hkv + sg.h) * D + col * kVec;
+    kr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kd + src));
+    vr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vd + src));
+    const int phys = p.v2p[sg.vstart + (ti >> lp)];
+    dst[j] = ((int64_t(phys) << lp) + (ti & (p.P - 1))) * D + col * kVec;
   }
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) {
-    if (dst[j] >= 0) {
-      __builtin_nontemporal_store(kr[j], reinterpret_cast<u32x4_t*>(kp + dst[j]));
-      __builtin_nontemporal_store(vr[j], reinterpret_cast<u32x4_t*>(vp + dst[j]));
-    }
+    __builtin_nontemporal_store(kr[j], reinterpret_cast<u32x4_t*>(kp + dst[j]));
+    __builtin_nontemporal_store(vr[j], reinterpret_cast<u32x4_t*>(vp + dst[j]));
   }
 }
 

@@ -45,11 +45,14 @@ class SegPagedLayer:
         self.k_pool = torch.empty((max(self.n_phys, 1), self.P, self.D), dtype=t,
                                   device=self.device)
         self.v_pool = torch.empty_like(self.k_pool)
-        Bn = len(self.ctx_len)
-        self.seg_table = torch.zeros((max(Bn, 1), self.Hkv, 2, 4), dtype=torch.int32,
-                                     device=self.device)
-        self.kv_len = torch.zeros((max(Bn, 1), self.Hkv), dtype=torch.int32, device=self.device)
-        self.v2p = torch.zeros((max(self.n_virt, 1),), dtype=torch.int32, device=self.device)
+        # one allocation, three adjacent tables: the build uploads them in a single copy
+        Bn = max(len(self.ctx_len), 1)
+        n_tab, n_kl = Bn * self.Hkv * 8, Bn * self.Hkv
+        tables = torch.zeros((n_tab + n_kl + max(self.n_virt, 1),), dtype=torch.int32,
+                             device=self.device)
+        self.seg_table = tables[:n_tab].view(Bn, self.Hkv, 2, 4)
+        self.kv_len = tables[n_tab:n_tab + n_kl].view(Bn, self.Hkv)
+        self.v2p = tables[n_tab + n_kl:]
         self.rebuild(k_dense, v_dense, fl, stream)
 
     def rebuild(self, k_dense: torch.Tensor, v_dense: torch.Tensor, free_pages,

@@ -115,8 +115,9 @@ sp_status segpaged_layout_tables(int32_t B, const int32_t* ctx_len, const int32_
  *   seg_table        : device int32 [B][Hkv][2][4]   (written)
  *   kv_len           : device int32 [B][Hkv]         (written)
  *   v2p              : device int32 [n_virt]         (written; n_virt = segpaged_plan_pages)
- * The tables are uploaded with a copy that completes before return; the scatter kernel runs
- * asynchronously on `stream`. Errors: SP_ERR_POOL_TOO_SMALL if n_free < n_virt,
+ * The tables are uploaded with a copy that completes before return (one copy when kv_len
+ * directly follows seg_table and v2p directly follows kv_len in memory, else three); the
+ * scatter kernel runs asynchronously on `stream`. Errors: SP_ERR_POOL_TOO_SMALL if n_free < n_virt,
  * SP_ERR_INVALID_ARG for duplicate or out-of-range free-list entries. */
 sp_status segpaged_build(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int32_t page_size,
                          const int32_t* ctx_len, const int32_t* q_len, const sp_head_policy* pol,

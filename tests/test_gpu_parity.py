@@ -126,6 +126,61 @@ def test_page_permutation_and_repeat_are_bitwise_identical():
     assert torch.equal(out1, out3)
 
 
+def _bits(x):
+    """Raw element bits of a device tensor or host array (bf16 has no numpy type)."""
+    if isinstance(x, torch.Tensor):
+        x = x.cpu()
+        return (x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)).numpy()
+    return x.view(np.int16) if x.dtype.itemsize == 2 else x.view(np.int32)
+
+
+def _check_pool(c, seg, v2p, k_pool, v_pool):
+    """Every stored (token, head) row of the pool equals its dense row, bit for bit."""
+    kp, vp, kd, vd = _bits(k_pool), _bits(v_pool), _bits(c.k), _bits(c.v)
+    row0 = np.concatenate([[0], np.cumsum(c.ctx_len)[:-1]])
+    for b in range(c.B):
+        for h in range(c.Hkv):
+            g = oracle.gather_positions(seg, v2p, c.P, b, h)
+            if not g:
+                continue
+            pos, page, slot = (np.array(t) for t in zip(*g))
+            np.testing.assert_array_equal(kp[page, slot], kd[row0[b] + pos, h])
+            np.testing.assert_array_equal(vp[page, slot], vd[row0[b] + pos, h])
+
+
+@pytest.mark.parametrize("name", ["tiny", "page16_bf16", "multi_request", "decode_g16"])
+def test_build_pool_bit_exact_with_adjacent_and_separate_tables(name):
+    """The build uploads the three tables in one copy when they are adjacent (the layer's
+    allocation) and in three otherwise; both give the oracle's tables and an exact pool,
+    including segments that end inside a 64-token copy unit."""
+    from head_aware_paged_segpaged_amd import binding
+    c = config_case(0) if name == "tiny" else dict(_edge_cases())[name]()
+    print("case build", name, flush=True)
+    seg_o, kvl_o, n_virt = oracle.plan_tables(c.ctx_len, c.q_len, c.policy, c.P)
+    _, layer = run_segpaged(c)
+    np.testing.assert_array_equal(layer.seg_table.cpu().numpy(), seg_o)
+    np.testing.assert_array_equal(layer.kv_len.cpu().numpy(), kvl_o)
+    _check_pool(c, seg_o, layer.v2p.cpu().numpy(), layer.k_pool, layer.v_pool)
+    # separate tables, another free list and a larger pool
+    n_phys = n_virt + 11
+    fl = np.random.default_rng(5).permutation(n_phys).astype(np.int32)
+    k, v = to_device(c.k, c.dtype), to_device(c.v, c.dtype)
+    kp = torch.empty((n_phys, c.P, c.D), dtype=k.dtype, device=DEV)
+    vp = torch.empty_like(kp)
+    seg = torch.full((c.B, c.Hkv, 2, 4), -7, dtype=torch.int32, device=DEV)
+    gap = torch.empty(3, dtype=torch.int32, device=DEV)  # keeps the tables apart
+    kvl = torch.full((c.B, c.Hkv), -7, dtype=torch.int32, device=DEV)
+    v2p = torch.full((n_virt,), -7, dtype=torch.int32, device=DEV)
+    binding.segpaged_build(c.dtype, c.D, c.P, c.ctx_len, c.q_len, c.policy, k, v, fl, n_phys,
+                           kp, vp, seg, kvl, v2p)
+    torch.cuda.synchronize()
+    del gap
+    np.testing.assert_array_equal(seg.cpu().numpy(), seg_o)
+    np.testing.assert_array_equal(kvl.cpu().numpy(), kvl_o)
+    np.testing.assert_array_equal(v2p.cpu().numpy(), fl[:n_virt])
+    _check_pool(c, seg_o, fl, kp, vp)
+
+
 @pytest.mark.parametrize("index", [0, 1])
 def test_dense_mask_baseline_matches_oracle(index):
     c = config_case(index)
