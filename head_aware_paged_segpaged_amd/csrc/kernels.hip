@@ -465,6 +465,28 @@ __device__ __forceinline__ bool in_mask(const KeyMask& m, int c, bool dual) {
   return dual ? (v || uint32_t(c - m.a1) < uint32_t(m.n1)) : v;
 }
 
+// The same mask as 64 bits, bit c for value position c (positions outside 0..63 are never
+// visible): built once per row and step, then each of a lane's 32 values costs two bit
+// operations (sign-extend bit c, then select the value's bits or -inf's) instead of a
+// subtract, compare and select per interval.
+__device__ __forceinline__ uint64_t range_bits(int a, int n) {
+  const int lo = max(a, 0), hi = min(a + n, 64);
+  if (hi <= lo) return 0ull;
+  const uint64_t ones = hi - lo >= 64 ? ~0ull : (1ull << (hi - lo)) - 1ull;
+  return ones << lo;
+}
+
+__device__ __forceinline__ uint64_t mask_bits(const KeyMask& m, bool dual) {
+  const uint64_t b = range_bits(m.a0, m.n0);
+  return dual ? b | range_bits(m.a1, m.n1) : b;
+}
+
+// x if bit c of `bits` is set, else -inf.
+__device__ __forceinline__ float keep_if(uint32_t bits, int c, float x) {
+  const uint32_t k = uint32_t(int32_t(bits << (31 - c)) >> 31);
+  return __uint_as_float((k & __float_as_uint(x)) | (~k & 0xff800000u));
+}
+
 // ---------------------------------------------------------------------------------------
 // Prefill: persistent, 256 threads, 128-row tiles.
 // ---------------------------------------------------------------------------------------
@@ -585,12 +607,13 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
                          (kind == SP_GLOBAL || last < sink || st.pos0 > pmax - window);
       if (kDense || !clear) {
         const bool dual = step_is_dual(st, kind, sink, window, pmin);
-        const KeyMask km = key_mask(st, p_row, kind, sink, window, dual, 4 * hh);
+        const uint64_t mb = mask_bits(key_mask(st, p_row, kind, sink, window, dual, 4 * hh), dual);
+        const uint32_t m_lo = uint32_t(mb), m_hi = uint32_t(mb >> 32);
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int c = 8 * (rr >> 2) + (rr & 3);
-          a0[rr] = in_mask(km, c, dual) ? a0[rr] : kNegInf;
-          a1[rr] = in_mask(km, 32 + c, dual) ? a1[rr] : kNegInf;
+          a0[rr] = keep_if(m_lo, c, a0[rr]);
+          a1[rr] = keep_if(m_hi, c, a1[rr]);  // value position 32 + c
         }
       }
     };
