@@ -107,6 +107,29 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Instruction interleave of one prefill step, for the machine scheduler: `pre` LDS reads, then
+// nA S^T MFMAs each followed by one LDS read, vA VALU and tA transcendental instructions, then
+// nC P*V MFMAs each followed by two LDS reads and vC VALU. On gfx950 a few independent VALU
+// instructions placed between MFMAs run almost for free, while the same work gathered into a
+// block between MFMA blocks adds its full length to the step.
+template <int nA, int vA, int tA, int nC, int vC, int pre>
+__device__ __forceinline__ void step_schedule() {
+  __builtin_amdgcn_sched_group_barrier(0x100, pre, 0);
+#pragma unroll
+  for (int m = 0; m < nA; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, vA, 0);
+    __builtin_amdgcn_sched_group_barrier(0x400, tA, 0);
+  }
+#pragma unroll
+  for (int m = 0; m < nC; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, vC, 0);
+  }
+}
+
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 __device__ __forceinline__ void set_error(uint8_t* ws, int code) {
@@ -728,9 +751,10 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     float mp = update_max(sp0, sp1);
     kv_barrier<0>();
 
-    // Iteration i: (A) S^T(i) on the matrix cores alongside the exponentials of step i-1;
-    // (B) P*V(i-1) alongside the row maximum of step i (after its mask); then O and l move to
-    // the new reference. K(i+1) and V(i) are in flight.
+    // Iteration i: S^T(i) on the matrix cores interleaved with the exponentials of step i-1,
+    // then P*V(i-1) (one basic block, instruction mix set by step_schedule); then the mask and
+    // row maximum of step i, and O and l move to the new reference if needed. K(i+1) and V(i)
+    // are in flight.
     auto run_step = [&](auto stage_c, int i) {
       constexpr int stg = decltype(stage_c)::value;  // i & 1
       issue_step<E, D, kDense, true, false>(p, w, kv, nxt, stg ? lk0 : lk1, nullptr);
@@ -740,8 +764,10 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
       qk(stg ? lk1 : lk0, sc0, sc1);
       F pb[2][16 / KPL];
       probs(sp0, sp1, mp, pb);
-      mask(cur, sc0, sc1);
       pv(stg ? lv0 : lv1, pb);
+      if constexpr (kBf16)  // 32 scores per lane: 32 FMA + 16 packs, 32 exponentials, 32 adds
+        step_schedule<2 * NQK, 48 / (2 * NQK), 32 / (2 * NQK), 4 * ND, 32 / (4 * ND), 4>();
+      mask(cur, sc0, sc1);
       mp = update_max(sc0, sc1);
       kv_barrier<0>();
       sp0 = sc0;
