@@ -575,9 +575,10 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     const WorkItem w = load_item(items, it);
     ItemKV kv;
     load_item_kv(p, w, kDense, kv, p.ws);
-    const int kind = uniform(pol[w.h * 3 + 0]);
-    const int sink = uniform(pol[w.h * 3 + 1]);
-    const int window = uniform(pol[w.h * 3 + 2]);
+    const int32_t* ph = pol + (w.b * p.Hkv + w.h) * 3;  // effective policy of (request, head)
+    const int kind = uniform(ph[0]);
+    const int sink = uniform(ph[1]);
+    const int window = uniform(ph[2]);
 
     // This lane's query row.
     const int r = wave * 32 + lq;
@@ -997,9 +998,10 @@ __global__ void __launch_bounds__(64) decode_kernel(AttnParams p) {
       load_item_kv(p, w, kDense, kv, p.ws);
       src = sub_source(w, kv, kDense, p.P);
     }
-    const int kind = uniform(pol[w.h * 3 + 0]);
-    const int sink = uniform(pol[w.h * 3 + 1]);
-    const int window = uniform(pol[w.h * 3 + 2]);
+    const int32_t* ph = pol + (w.b * p.Hkv + w.h) * 3;  // effective policy of (request, head)
+    const int kind = uniform(ph[0]);
+    const int sink = uniform(ph[1]);
+    const int window = uniform(ph[2]);
     const int rows = w.nq * p.G;
 
     // Query row of this lane's MFMA column.

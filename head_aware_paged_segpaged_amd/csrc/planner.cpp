@@ -55,7 +55,7 @@ sp_status check_lengths_policy(int32_t B, const int32_t* ctx_len, const int32_t*
   if (pol == nullptr) return SP_ERR_INVALID_ARG;
   for (int32_t h = 0; h < Hkv; ++h) {
     if (pol[h].kind == SP_GLOBAL) continue;
-    if (pol[h].kind != SP_LOCAL) return SP_ERR_INVALID_ARG;
+    if (pol[h].kind != SP_LOCAL && pol[h].kind != SP_LOCAL_ADAPTIVE) return SP_ERR_INVALID_ARG;
     if (pol[h].sink < 0 || pol[h].window < 1) return SP_ERR_INVALID_ARG;
   }
   int64_t tot_ctx = 0, tot_q = 0;
@@ -85,8 +85,14 @@ sp_status check_shape(const Shape& s) {
   return SP_OK;
 }
 
-int head_segments(const sp_head_policy& pol, int32_t L, int32_t q, int32_t out_pos[2],
+sp_head_policy effective_policy(const sp_head_policy& pol, int32_t L) {
+  if (pol.kind != SP_LOCAL_ADAPTIVE) return pol;
+  return sp_head_policy{SP_LOCAL, pol.sink, std::max<int32_t>(1, L / pol.window)};
+}
+
+int head_segments(const sp_head_policy& pol_in, int32_t L, int32_t q, int32_t out_pos[2],
                   int32_t out_ntok[2]) {
+  const sp_head_policy pol = effective_policy(pol_in, L);
   if (L <= 0) return 0;
   if (pol.kind == SP_GLOBAL) {
     out_pos[0] = 0;
@@ -166,7 +172,7 @@ uint64_t shape_signature(const Shape& s, int32_t slots_prefill, int32_t slots_de
                                                    uint32_t(s.q_len[b]));
   for (int32_t i = 0; i < s.Hkv; ++i) {
     h = fnv(h, uint64_t(uint32_t(s.pol[i].kind)));
-    if (s.pol[i].kind == SP_LOCAL)
+    if (s.pol[i].kind != SP_GLOBAL)
       h = fnv(h, (uint64_t(uint32_t(s.pol[i].sink)) << 32) | uint32_t(s.pol[i].window));
   }
   return h;
@@ -314,7 +320,7 @@ sp_status make_plan(const Shape& s, int32_t slots_prefill, int32_t slots_decode,
           const int32_t nt = std::min(bq, nq - t0);
           const int32_t pmin = p0 + t0, pmax = pmin + nt - 1;
           Range ra, rb;
-          tile_ranges(s, hl, s.pol[h], pmin, pmax, L, &ra, &rb);
+          tile_ranges(s, hl, effective_policy(s.pol[h], L), pmin, pmax, L, &ra, &rb);
           Tile t{};
           WorkItem& w = t.w;
           w.b = b;
@@ -354,11 +360,16 @@ sp_status make_plan(const Shape& s, int32_t slots_prefill, int32_t slots_decode,
   make_queues(pre_items, &out->prefill, hd.prefill_q);
   make_queues(dec_items, &out->decode, hd.decode_q);
   out->combine = combine;
-  out->policy.resize(size_t(s.Hkv) * 3);
-  for (int32_t h = 0; h < s.Hkv; ++h) {
-    out->policy[h * 3 + 0] = s.pol[h].kind;
-    out->policy[h * 3 + 1] = s.pol[h].kind == SP_LOCAL ? s.pol[h].sink : 0;
-    out->policy[h * 3 + 2] = s.pol[h].kind == SP_LOCAL ? s.pol[h].window : 1;
+  // The kernels' policy table: one effective (kind, sink, window) per (request, KV head).
+  out->policy.resize(size_t(std::max(s.B, 1)) * s.Hkv * 3);
+  for (int32_t b = 0; b < s.B; ++b) {
+    for (int32_t h = 0; h < s.Hkv; ++h) {
+      const sp_head_policy e = effective_policy(s.pol[h], s.ctx_len[b]);
+      int32_t* d = &out->policy[(size_t(b) * s.Hkv + h) * 3];
+      d[0] = e.kind;
+      d[1] = e.kind == SP_LOCAL ? e.sink : 0;
+      d[2] = e.kind == SP_LOCAL ? e.window : 1;
+    }
   }
 
   hd.magic = kMagic;

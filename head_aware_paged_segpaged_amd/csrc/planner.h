@@ -44,6 +44,9 @@ sp_status check_lengths_policy(int32_t B, const int32_t* ctx_len, const int32_t*
                                int32_t Hkv, const sp_head_policy* pol);
 sp_status check_shape(const Shape& s);
 
+// Policy of one head for a request of context length L: an SP_LOCAL_ADAPTIVE head becomes a
+// LOCAL head with window max(1, L / divisor); other heads are returned unchanged.
+sp_head_policy effective_policy(const sp_head_policy& pol, int32_t L);
 // Segments of one (request, KV head) following the layout rules of include/segpaged.h.
 int head_segments(const sp_head_policy& pol, int32_t L, int32_t q, int32_t out_pos[2],
                   int32_t out_ntok[2]);

@@ -26,6 +26,8 @@
  *   hq / G (contiguous groups).
  * - Visibility of key position j to a query at position p:
  *     GLOBAL: j <= p;   LOCAL: j <= p and (j < sink or j > p - window).
+ *   A LOCAL_ADAPTIVE head is a LOCAL head whose window, for request b, is
+ *   max(1, ctx_len[b] / window) (integer division; its `window` field is the divisor).
  * - Dense K/V are token-major with requests concatenated: [sum(ctx_len), Hkv, D], request b's
  *   rows start at sum_{b'<b} ctx_len[b']. Q and O are [sum(q_len), Hq, D]. Rows are dense
  *   (row stride Hkv*D or Hq*D elements).
@@ -81,14 +83,17 @@ typedef enum sp_status {
 
 typedef enum sp_dtype { SP_BF16 = 0, SP_F32 = 1 } sp_dtype;
 
-typedef enum sp_head_kind { SP_GLOBAL = 0, SP_LOCAL = 1 } sp_head_kind;
+typedef enum sp_head_kind { SP_GLOBAL = 0, SP_LOCAL = 1, SP_LOCAL_ADAPTIVE = 2 } sp_head_kind;
 
 /* One per KV head (page "RedKnot head classification": head types, defaults window 512 and
- * sink 4). `sink` and `window` are ignored for SP_GLOBAL heads. */
+ * sink 4). `sink` and `window` are ignored for SP_GLOBAL heads. SP_LOCAL_ADAPTIVE follows the
+ * same page's passage on windows that adapt to each request's context length (its example:
+ * half the context): the head is LOCAL with window max(1, ctx_len[b] / window) for request b,
+ * so `window` is a divisor >= 1. Any other kind is SP_ERR_INVALID_ARG. */
 typedef struct sp_head_policy {
-  int32_t kind;   /* sp_head_kind */
-  int32_t sink;   /* S >= 0       */
-  int32_t window; /* W >= 1       */
+  int32_t kind;   /* sp_head_kind                         */
+  int32_t sink;   /* S >= 0                               */
+  int32_t window; /* W >= 1 (SP_LOCAL_ADAPTIVE: divisor >= 1) */
 } sp_head_policy;
 
 /* Human-readable name of a status code. Never NULL. */

@@ -12,7 +12,9 @@ What it computes, and from which passage of the RedKnot pages:
   the cosine check against a dense-plus-mask baseline must exceed 0.99998). GLOBAL heads read
   the whole prefix and LOCAL heads read the first S sink tokens plus a recent window of W
   tokens (same page, sections 1-3; page "RedKnot head classification", the four head types,
-  defaults window 512 and sink 4). So the oracle is that definition written out.
+  defaults window 512 and sink 4). So the oracle is that definition written out. An adaptive
+  LOCAL head has window max(1, L // d) for a request of context length L (page "RedKnot head
+  classification", windows that scale with the request's context).
 * ``plan``: the per-(request, KV head) segment list, true KV length, virtual page ids and the
   virtual-to-physical map (page "RedKnot SegPagedAttention runtime design", section 3: one
   page table per (layer, head, segment) over contiguous virtual pages, a shared physical
@@ -25,4 +27,5 @@ example). Nothing here is "parity unpinned".
 """
 
 from .attention import GLOBAL, LOCAL, attention, attention_rows, to_f64, visible  # noqa: F401
-from .plan import gather_positions, plan_tables, segments  # noqa: F401
+from .plan import (LOCAL_ADAPTIVE, gather_positions, head_policy, plan_tables,  # noqa: F401
+                   segments)

@@ -9,7 +9,9 @@ h = hq // G (G = Hq / Hkv, contiguous groups). The keys it may see are
 
 * GLOBAL head: every position j with j <= p;
 * LOCAL head (sink S, window W): j <= p and (j < S or j > p - W), i.e. the first S tokens
-  plus the W most recent tokens up to and including p.
+  plus the W most recent tokens up to and including p;
+* adaptive LOCAL head: a LOCAL head with W = max(1, L // d) for the request's context length
+  L (``plan.head_policy``).
 
 O[b, t, hq] = sum_j softmax_j(scale * <Q, K_j>) V_j over the visible j, with the softmax
 taken over the visible set only (masked logits are -inf).
@@ -19,8 +21,7 @@ from __future__ import annotations
 
 import numpy as np
 
-GLOBAL = 0
-LOCAL = 1
+from .plan import GLOBAL, LOCAL, head_policy
 
 # Rows of one (request, head) are processed a slice at a time so that the dense logits stay
 # within a bounded amount of memory. Each output row is independent of the others, so this
@@ -73,7 +74,8 @@ def attention_rows(q, k, v, ctx_len, q_len, policy, Hq: int, Hkv: int, scale: fl
 
     ``q`` is [sum(q_len), Hq, D] and ``k``/``v`` are [sum(ctx_len), Hkv, D] (token-major,
     requests concatenated); bf16 inputs are uint16 bit patterns. ``policy`` is [Hkv, 3] =
-    (kind, sink, window). ``tokens`` indexes the request's query chunk (default: all).
+    (kind, sink, window), kinds GLOBAL, LOCAL or LOCAL_ADAPTIVE. ``tokens`` indexes the
+    request's query chunk (default: all).
     """
     ctx_len = np.asarray(ctx_len, dtype=np.int64)
     q_len = np.asarray(q_len, dtype=np.int64)
@@ -86,7 +88,7 @@ def attention_rows(q, k, v, ctx_len, q_len, policy, Hq: int, Hkv: int, scale: fl
     if tokens is None:
         tokens = np.arange(nq)
     tokens = np.asarray(tokens, dtype=np.int64)
-    kind, sink, window = (int(x) for x in policy[h])
+    kind, sink, window = head_policy(*(int(x) for x in policy[h]), L)
     q_rows = to_f64(q[q0 + tokens, hq, :], dtype)
     k_head = to_f64(k[kv0:kv0 + L, h, :], dtype)
     v_head = to_f64(v[kv0:kv0 + L, h, :], dtype)

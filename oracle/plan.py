@@ -23,6 +23,10 @@ Readings taken where the pages are silent (one layer per call):
 * An unused segment slot reads (pos_start 0, n_tok 0, vpage_start = running total, n_pages 0).
 * v2p[v] = free_pages[v]: physical pages are taken from the caller's free list in order.
 * kv_len[b, h] = total stored tokens of the head.
+* An adaptive LOCAL head (page "RedKnot head classification", the passage on windows that
+  scale with each request's context length, whose example is half the context) is a LOCAL
+  head whose window for a request of context length L is max(1, L // d), d being its
+  configured divisor; L is the request's whole context at this call, query chunk included.
 """
 
 from __future__ import annotations
@@ -31,6 +35,15 @@ import numpy as np
 
 GLOBAL = 0
 LOCAL = 1
+LOCAL_ADAPTIVE = 2
+
+
+def head_policy(kind: int, sink: int, window: int, L: int):
+    """(kind, sink, window) of one head for a request of context length L: an adaptive LOCAL
+    head (``window`` = divisor d) becomes LOCAL with window max(1, L // d)."""
+    if kind == LOCAL_ADAPTIVE:
+        return LOCAL, sink, max(1, L // window)
+    return kind, sink, window
 
 
 def segments(kind: int, sink: int, window: int, L: int, q: int):
@@ -61,7 +74,7 @@ def plan_tables(ctx_len, q_len, policy, P: int):
         L = int(ctx_len[b])
         q = int(q_len[b])
         for h in range(Hkv):
-            kind, sink, window = (int(x) for x in policy[h])
+            kind, sink, window = head_policy(*(int(x) for x in policy[h]), L)
             segs = segments(kind, sink, window, L, q)
             total = 0
             for s in range(2):

@@ -55,8 +55,11 @@ def test_layout_tables_random_against_oracle():
         P = int(rng.choice([16, 32, 64, 128, 256]))
         ctx = rng.integers(0, 700, size=B)
         q = np.array([rng.integers(0, c + 1) for c in ctx])
-        pol = [(int(rng.integers(0, 2)), int(rng.integers(0, 70)), int(rng.integers(1, 600)))
-               for _ in range(Hkv)]
+        pol = []
+        for _ in range(Hkv):
+            kind = int(rng.integers(0, 3))  # GLOBAL, LOCAL, LOCAL_ADAPTIVE (window = divisor)
+            pol.append((kind, int(rng.integers(0, 70)),
+                        int(rng.integers(1, 9 if kind == 2 else 600))))
         seg, kvl = sp.segpaged_layout_tables(ctx, q, pol, P)
         seg_o, kvl_o, n_virt = plan_tables(ctx, q, pol, P)
         np.testing.assert_array_equal(seg, seg_o)
@@ -78,6 +81,9 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert _err(sp.segpaged_plan_pages, [10], [1], [(1, -1, 4)], 16) == E.SP_ERR_INVALID_ARG
     assert _err(sp.segpaged_plan_pages, [10], [1], [(1, 2, 0)], 16) == E.SP_ERR_INVALID_ARG
     assert _err(sp.segpaged_plan_pages, [10], [1], [(7, 2, 3)], 16) == E.SP_ERR_INVALID_ARG
+    assert _err(sp.segpaged_plan_pages, [10], [1], [(2, 2, 0)], 16) == E.SP_ERR_INVALID_ARG
+    assert _err(sp.segpaged_plan_pages, [10], [1], [(2, -1, 2)], 16) == E.SP_ERR_INVALID_ARG
+    assert _err(sp.segpaged_plan_pages, [10], [1], [(3, 2, 2)], 16) == E.SP_ERR_INVALID_ARG
     assert _err(sp.segpaged_plan_pages, [10], [1], pol, 48) == E.SP_ERR_UNSUPPORTED
     assert _err(sp.segpaged_plan_pages, [10], [1], pol, 8) == E.SP_ERR_UNSUPPORTED
     # attention shape checks run before any device query

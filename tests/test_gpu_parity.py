@@ -12,11 +12,11 @@ import torch
 import oracle
 from tests.helpers import (COS_MIN, DEV, MAXABS, assert_parity, run_dense_mask, run_segpaged,
                            sample_rows, to_device, to_f64)
-from workloads import GLOBAL, LOCAL, config_case, custom_case, free_list
+from workloads import GLOBAL, LOCAL, LOCAL_ADAPTIVE, config_case, custom_case, free_list
 
 pytestmark = pytest.mark.gpu
 
-G_, L_ = GLOBAL, LOCAL
+G_, L_, A_ = GLOBAL, LOCAL, LOCAL_ADAPTIVE
 
 
 def _oracle(c, scale=None):
@@ -88,6 +88,10 @@ def _edge_cases():
         ("decode_g16", lambda: mk(31, dtype="bf16", Hq=16, Hkv=1, D=128, P=64,
                                   ctx_len=[5000, 63, 64, 65], q_len=[1, 1, 1, 1],
                                   policy=[(L_, 4, 512)])),
+        # windows that follow each request's context length: 450, 150, 1000 and 180, 60, 400
+        ("adaptive_windows", lambda: mk(32, dtype="bf16", Hq=12, Hkv=3, D=128, P=64,
+                                        ctx_len=[900, 300, 2000], q_len=[100, 1, 257],
+                                        policy=[(A_, 4, 2), (A_, 0, 5), (G_, 0, 1)])),
     ]
 
 
@@ -291,7 +295,27 @@ def _random_cases(n=16, seed=2024):
     return out
 
 
-@pytest.mark.parametrize("args", _random_cases(), ids=lambda a: "seed%d" % a["seed"])
+def _adaptive_cases(n=6, seed=4048):
+    """Random shapes whose LOCAL heads take windows from each request's context length."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        Hkv = int(rng.choice([1, 2, 3]))
+        G = int(rng.choice([1, 4, 8]))
+        B = int(rng.integers(1, 4))
+        ctx = rng.integers(1, 2500, B)
+        q = np.minimum(ctx, rng.choice([1, 3, 64, 300], B))
+        pol = [(A_, int(rng.choice([0, 4])), int(rng.choice([1, 2, 3, 8]))) for _ in range(Hkv)]
+        if Hkv > 1:
+            pol[0] = (G_, 0, 1)
+        out.append(dict(seed=600 + i, dtype="f32" if i == 5 else "bf16", Hq=Hkv * G, Hkv=Hkv,
+                        D=int(rng.choice([64, 128])), P=int(rng.choice([16, 64, 128])),
+                        ctx_len=list(ctx), q_len=list(q), policy=pol))
+    return out
+
+
+@pytest.mark.parametrize("args", _random_cases() + _adaptive_cases(),
+                         ids=lambda a: "seed%d" % a["seed"])
 def test_random_shapes_against_oracle(args):
     # Seeded random shapes across dtypes, head dims, GQA groups, page sizes, request mixes
     # (decode and prefill together) and policies.

@@ -217,3 +217,39 @@ def test_rows_subset_matches_full():
     sub = attention_rows(c.q, c.k, c.v, c.ctx_len, c.q_len, c.policy, 4, 2, c.scale, c.dtype,
                          b=1, hq=3, tokens=[0, 5, 16])
     np.testing.assert_array_equal(sub, full[11 + np.array([0, 5, 16]), 3])
+
+
+def test_adaptive_window_against_brute_force():
+    # Adaptive LOCAL heads (window = L // d per request) against the pure-Python loops, which
+    # take the window the page's rule gives for each request, computed here by hand.
+    from oracle import LOCAL_ADAPTIVE
+    ctx, ql = [40, 23, 9], [9, 23, 1]
+    pol = [(LOCAL_ADAPTIVE, 2, 4), (LOCAL_ADAPTIVE, 0, 2), (GLOBAL, 0, 1)]
+    windows = {0: [10, 5, 2], 1: [20, 11, 4]}  # 40 // 4, 23 // 4, 9 // 4; 40 // 2, ...
+    c = custom_case(77, dtype="f32", Hq=6, Hkv=3, D=5, P=16, ctx_len=ctx, q_len=ql, policy=pol)
+    out = attention(c.q, c.k, c.v, c.ctx_len, c.q_len, c.policy, 6, 3, c.scale, c.dtype)
+    q0 = kv0 = 0
+    for b in range(3):
+        L, nq = ctx[b], ql[b]
+        for hq in range(6):
+            h = hq // 2
+            kind, sink = (LOCAL, pol[h][1]) if h < 2 else (GLOBAL, 0)
+            W = windows[h][b] if h < 2 else 1
+            k_rows = [list(map(float, r)) for r in c.k[kv0:kv0 + L, h]]
+            v_rows = [list(map(float, r)) for r in c.v[kv0:kv0 + L, h]]
+            for t in range(nq):
+                ref = brute.attention_row(list(map(float, c.q[q0 + t, hq])), k_rows, v_rows,
+                                          L - nq + t, kind, sink, W, c.scale)
+                np.testing.assert_allclose(out[q0 + t, hq], ref, rtol=1e-12, atol=1e-14)
+        q0 += nq
+        kv0 += L
+
+
+def test_adaptive_window_divisor_one_equals_global():
+    from oracle import LOCAL_ADAPTIVE
+    base = dict(dtype="bf16", Hq=2, Hkv=1, D=8, P=16, ctx_len=[45, 12], q_len=[30, 12])
+    a = custom_case(10, policy=[(LOCAL_ADAPTIVE, 3, 1)], **base)
+    b = custom_case(10, policy=[(GLOBAL, 0, 1)], **base)
+    oa = attention(a.q, a.k, a.v, a.ctx_len, a.q_len, a.policy, 2, 1, a.scale, a.dtype)
+    ob = attention(b.q, b.k, b.v, b.ctx_len, b.q_len, b.policy, 2, 1, b.scale, b.dtype)
+    np.testing.assert_array_equal(oa, ob)

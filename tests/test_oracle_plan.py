@@ -122,3 +122,35 @@ def test_empty_and_degenerate_heads():
     assert kv.tolist() == [[0], [5]]
     assert seg[0, 0].tolist() == [[0, 0, 0, 0], [0, 0, 0, 0]]
     assert seg[1, 0].tolist() == [[0, 5, 0, 1], [0, 0, 1, 0]]
+
+
+def test_adaptive_window_tables_worked_example():
+    # Page "RedKnot head classification": a LOCAL window may follow the request's context
+    # length, its example being half of it. Two requests, sink 4, divisor 2, pages of 16:
+    #   L = 1000, q = 100 -> W = 500, R0 = 1000 - 100 - 500 + 1 = 401:
+    #     segments (0, 4) -> 1 page, (401, 599) -> ceil(599 / 16) = 38 pages.
+    #   L = 300, q = 1 -> W = 150, R0 = 300 - 1 - 150 + 1 = 150:
+    #     segments (0, 4) -> 1 page, (150, 150) -> ceil(150 / 16) = 10 pages.
+    # Virtual pages in (request, head, segment) order: 0, 1 | 39, 40; 50 in total.
+    from oracle import LOCAL_ADAPTIVE
+    seg, kv_len, n_virt = plan_tables([1000, 300], [100, 1], [(LOCAL_ADAPTIVE, 4, 2)], 16)
+    np.testing.assert_array_equal(seg[0, 0], [[0, 4, 0, 1], [401, 599, 1, 38]])
+    np.testing.assert_array_equal(seg[1, 0], [[0, 4, 39, 1], [150, 150, 40, 10]])
+    np.testing.assert_array_equal(kv_len, [[603], [154]])
+    assert n_virt == 50
+
+
+def test_adaptive_window_divisor_one_stores_like_global():
+    # Divisor 1 gives W = L, so every query of the chunk sees the whole prefix: the head's
+    # storage must be a GLOBAL head's, for any sink and chunk length.
+    from oracle import LOCAL_ADAPTIVE
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        B = int(rng.integers(1, 4))
+        L = rng.integers(1, 500, B)
+        q = np.array([int(rng.integers(1, x + 1)) for x in L])
+        S = int(rng.integers(0, 9))
+        a = plan_tables(L, q, [(LOCAL_ADAPTIVE, S, 1)], 32)
+        g = plan_tables(L, q, [(GLOBAL, 0, 1)], 32)
+        np.testing.assert_array_equal(a[0], g[0])
+        np.testing.assert_array_equal(a[1], g[1])

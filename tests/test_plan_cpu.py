@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from head_aware_paged_segpaged_amd import segpaged_attention_plan_host
-from workloads import GLOBAL, LOCAL, config_case, custom_case
+from workloads import GLOBAL, LOCAL, LOCAL_ADAPTIVE, config_case, custom_case
 
 STEP = 64          # stored slots per KV step
 TILE_ROWS = 128    # rows of a prefill item
@@ -50,7 +50,7 @@ def item_slots(it):
 def visible_slots(case, b, h, t0, nq):
     """(segment, slot) of every stored token some query t0 .. t0+nq-1 of request b sees."""
     L, q = int(case.ctx_len[b]), int(case.q_len[b])
-    kind, sink, window = (int(x) for x in case.policy[h])
+    kind, sink, window = oracle.head_policy(*(int(x) for x in case.policy[h]), L)
     segs = oracle.segments(kind, sink, window, L, q)
     p = np.arange(L - q + t0, L - q + t0 + nq)
     out = set()
@@ -126,8 +126,11 @@ def test_plan_random_shapes():
         q = np.minimum(ctx, rng.choice([1, 2, 7, 64, 300], B))
         pol = []
         for _ in range(Hkv):
-            if rng.random() < 0.4:
+            r = rng.random()
+            if r < 0.3:
                 pol.append((GLOBAL, 0, 1))
+            elif r < 0.5:  # window = context length // divisor, per request
+                pol.append((LOCAL_ADAPTIVE, int(rng.choice([0, 4])), int(rng.choice([1, 2, 5, 40]))))
             else:
                 pol.append((LOCAL, int(rng.choice([0, 1, 4, 70])), int(rng.choice([1, 33, 64, 500]))))
         c = custom_case(100 + trial, dtype="bf16", Hq=Hkv * G, Hkv=Hkv, D=64, P=P,

@@ -9,6 +9,7 @@ from .synth import (  # noqa: F401
     CONFIGS,
     GLOBAL,
     LOCAL,
+    LOCAL_ADAPTIVE,
     Case,
     config_case,
     custom_case,

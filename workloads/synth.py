@@ -35,6 +35,7 @@ import numpy as np
 
 GLOBAL = 0
 LOCAL = 1
+LOCAL_ADAPTIVE = 2  # LOCAL with window = context length // divisor
 
 CHUNK = 1 << 22
 
