@@ -35,6 +35,11 @@ EVENT_EVERY = 4             # main-kernel events on every 4th timed step
 BUILD_RUNS = 5              # the build's time is the median of this many rebuilds
 
 
+def head_window(kind: int, window: int, L: int) -> int:
+    """LOCAL window of a head for a request of context length L (kind 2: L // divisor)."""
+    return max(1, L // window) if kind == 2 else window
+
+
 def visible_counts(case) -> np.ndarray:
     """Visible (query, key) pairs per (request, KV head), one query head's worth."""
     out = np.zeros((case.B, case.Hkv), dtype=np.float64)
@@ -43,6 +48,7 @@ def visible_counts(case) -> np.ndarray:
         p = np.arange(L - nq, L, dtype=np.int64)
         for h in range(case.Hkv):
             kind, S, W = (int(x) for x in case.policy[h])
+            W = head_window(kind, W, L)
             if kind == 0:
                 n = p + 1
             else:
@@ -121,6 +127,7 @@ def cpu_oracle_sample(case, budget_rows: int):
         L, nq = int(case.ctx_len[b]), int(case.q_len[b])
         p = L - nq + toks
         kind, S, W = (int(x) for x in case.policy[hq // G])
+        W = head_window(kind, W, L)
         if kind == 0:
             pairs += float((p + 1).sum())
         else:
@@ -135,7 +142,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=1,
-                    help="workload index (0-5; 5 = the 32K-128K slice of the decode workload); "
+                    help="workload index (0-6; 5 = the 32K-128K slice of the decode workload, "
+                         "6 = the decode workload with context-adaptive LOCAL windows); "
                          "default 1")
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="rows of the CPU-oracle sample (default sized for about 10-30 s)")
@@ -341,6 +349,8 @@ def main() -> int:
                    "global_kv_heads": [int(h) for h in np.nonzero(case.policy[:, 0] == 0)[0]],
                    "local_sink_window": [int(case.policy[:, 1].max()),
                                          int(case.policy[:, 2].max())],
+                   "local_window_rule": ("context length // %d" % int(case.policy[:, 2].max())
+                                         if (case.policy[:, 0] == 2).any() else "fixed"),
                    "gqa_group": G},
         "gbps": round(gbps, 1),
         "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),

@@ -235,7 +235,7 @@ def test_decode_repeat_is_bitwise_identical():
     assert layer.check() == 0
 
 
-@pytest.mark.parametrize("index,budget", [(2, 48), (3, 24), (4, 24), (5, 16)])
+@pytest.mark.parametrize("index,budget", [(2, 48), (3, 24), (4, 24), (5, 16), (6, 16)])
 def test_full_size_workload_sampled_rows(index, budget):
     # The full workloads, planned for this device exactly as the benchmark runs them: page
     # tables bit-exact, two heads' pool pages bit-exact, and seeded sampled output rows against

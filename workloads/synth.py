@@ -92,6 +92,11 @@ CONFIGS = [
     dict(name="qwen3_32b_decode_b64_32k_128k", dtype="bf16", Hq=64, Hkv=8, D=128, P=64, B=64,
          L=("log_uniform", 32768, 131072), q=("fixed", 1), globals=("draw", 2),
          sink=4, window=512, q_std=1.0 / math.sqrt(128), kv_std=1.0),
+    # The decode workload with LOCAL windows that follow each request's context, at half of
+    # it (the head classification page's example): `window` is then the divisor.
+    dict(name="qwen3_32b_decode_b64_4k_128k_half_window", dtype="bf16", Hq=64, Hkv=8, D=128,
+         P=64, B=64, L=("log_uniform", 4096, 131072), q=("fixed", 1), globals=("draw", 2),
+         sink=4, window=2, local_kind=LOCAL_ADAPTIVE, q_std=1.0 / math.sqrt(128), kv_std=1.0),
 ]
 
 
@@ -144,9 +149,10 @@ def _draw_tensor(seed: int, tensor_id: int, shape, std: float, dtype: str) -> np
     return x.reshape(shape)
 
 
-def _policy_table(Hkv: int, global_heads, sink: int, window: int) -> np.ndarray:
+def _policy_table(Hkv: int, global_heads, sink: int, window: int,
+                  local_kind: int = LOCAL) -> np.ndarray:
     pol = np.empty((Hkv, 3), dtype=np.int32)
-    pol[:, 0] = LOCAL
+    pol[:, 0] = local_kind
     pol[:, 1] = sink
     pol[:, 2] = window
     for h in global_heads:
@@ -177,7 +183,7 @@ def config_case(index: int, seed: int | None = None, with_tensors: bool = True) 
         ghs = list(gv)
     else:
         ghs = sorted(int(h) for h in rng.choice(cfg["Hkv"], gv, replace=False))
-    pol = _policy_table(cfg["Hkv"], ghs, cfg["sink"], cfg["window"])
+    pol = _policy_table(cfg["Hkv"], ghs, cfg["sink"], cfg["window"], cfg.get("local_kind", LOCAL))
     case = Case(name=cfg["name"], dtype=cfg["dtype"], B=B, Hq=cfg["Hq"], Hkv=cfg["Hkv"],
                 D=cfg["D"], P=cfg["P"], ctx_len=ctx, q_len=q, policy=pol,
                 scale=1.0 / math.sqrt(cfg["D"]), seed=seed)
