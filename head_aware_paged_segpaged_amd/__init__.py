@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     SP_F32,
     SP_GLOBAL,
     SP_LOCAL,
+    SP_LOCAL_ADAPTIVE,
     HipEvent,
     SegPagedError,
     lib,

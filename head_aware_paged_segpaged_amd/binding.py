@@ -29,6 +29,7 @@ SP_BF16 = 0
 SP_F32 = 1
 SP_GLOBAL = 0
 SP_LOCAL = 1
+SP_LOCAL_ADAPTIVE = 2
 
 EXPORTED = [
     "segpaged_status_string",
