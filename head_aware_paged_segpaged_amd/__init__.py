@@ -21,11 +21,14 @@ from .binding import (  # noqa: F401
     segpaged_attention_profiled,
     segpaged_attention_workspace_size,
     segpaged_build,
+    segpaged_build_layers,
     segpaged_dense_mask_attention,
     segpaged_dense_mask_plan,
     segpaged_dense_mask_workspace_size,
     segpaged_layout_tables,
+    segpaged_layout_tables_layers,
     segpaged_plan_pages,
+    segpaged_plan_pages_layers,
     status_string,
 )
-from .runtime import DenseMaskLayer, SegPagedLayer  # noqa: F401
+from .runtime import DenseMaskLayer, SegPagedLayer, SegPagedLayers  # noqa: F401

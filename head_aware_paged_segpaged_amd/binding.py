@@ -34,8 +34,11 @@ SP_LOCAL_ADAPTIVE = 2
 EXPORTED = [
     "segpaged_status_string",
     "segpaged_plan_pages",
+    "segpaged_plan_pages_layers",
     "segpaged_layout_tables",
+    "segpaged_layout_tables_layers",
     "segpaged_build",
+    "segpaged_build_layers",
     "segpaged_attention_workspace_size",
     "segpaged_attention_plan",
     "segpaged_attention",
@@ -64,6 +67,11 @@ _SIGS = {
     "segpaged_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "segpaged_plan_pages": (_i32, [_i32, _vp, _vp, _i32, _vp, _i32, ctypes.POINTER(_i64)]),
     "segpaged_layout_tables": (_i32, [_i32, _vp, _vp, _i32, _vp, _i32, _vp, _vp]),
+    "segpaged_plan_pages_layers": (_i32, [_i32, _i32, _vp, _vp, _i32, _vp, _i32,
+                                          ctypes.POINTER(_i64)]),
+    "segpaged_layout_tables_layers": (_i32, [_i32, _i32, _vp, _vp, _i32, _vp, _i32, _vp, _vp]),
+    "segpaged_build_layers": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                                     _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "segpaged_build": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                               _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "segpaged_attention_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
@@ -177,6 +185,49 @@ def segpaged_build(dtype, D: int, page_size: int, ctx_len, q_len, policy, k_dens
                                 _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
                                 _dev(seg_table, "seg_table"), _dev(kv_len, "kv_len"),
                                 _dev(v2p, "v2p"), _stream(stream)), "segpaged_build")
+
+
+def _layers_policy(policy):
+    """[n_layers][Hkv][3] int32 host policies."""
+    p = _host_i32(policy)
+    if p.ndim != 3 or p.shape[2] != 3:
+        raise ValueError("policy must be [n_layers][Hkv][3]")
+    return p
+
+
+def segpaged_plan_pages_layers(ctx_len, q_len, policy, page_size: int) -> int:
+    c, q, p = _host_i32(ctx_len), _host_i32(q_len), _layers_policy(policy)
+    out = _i64(0)
+    _check(lib().segpaged_plan_pages_layers(p.shape[0], len(c), _ptr(c), _ptr(q), p.shape[1],
+                                            _ptr(p), page_size, ctypes.byref(out)),
+           "segpaged_plan_pages_layers")
+    return int(out.value)
+
+
+def segpaged_layout_tables_layers(ctx_len, q_len, policy, page_size: int):
+    c, q, p = _host_i32(ctx_len), _host_i32(q_len), _layers_policy(policy)
+    n_layers, B, Hkv = p.shape[0], len(c), p.shape[1]
+    seg = np.zeros((n_layers, B, Hkv, 2, 4), dtype=np.int32)
+    kvl = np.zeros((n_layers, B, Hkv), dtype=np.int32)
+    _check(lib().segpaged_layout_tables_layers(n_layers, B, _ptr(c), _ptr(q), Hkv, _ptr(p),
+                                               page_size, seg.ctypes.data_as(_vp),
+                                               kvl.ctypes.data_as(_vp)),
+           "segpaged_layout_tables_layers")
+    return seg, kvl
+
+
+def segpaged_build_layers(dtype, D: int, page_size: int, ctx_len, q_len, policy, k_dense,
+                          v_dense, free_pages, n_phys: int, k_pool, v_pool, seg_table, kv_len,
+                          v2p, stream=None) -> None:
+    c, q, p = _host_i32(ctx_len), _host_i32(q_len), _layers_policy(policy)
+    fl = _host_i32(free_pages)
+    _check(lib().segpaged_build_layers(_dtype_code(dtype), p.shape[0], len(c), p.shape[1], D,
+                                       page_size, _ptr(c), _ptr(q), _ptr(p),
+                                       _dev(k_dense, "k_dense"), _dev(v_dense, "v_dense"),
+                                       _ptr(fl), fl.size, n_phys, _dev(k_pool, "k_pool"),
+                                       _dev(v_pool, "v_pool"), _dev(seg_table, "seg_table"),
+                                       _dev(kv_len, "kv_len"), _dev(v2p, "v2p"),
+                                       _stream(stream)), "segpaged_build_layers")
 
 
 def segpaged_attention_workspace_size(dtype, Hq: int, Hkv: int, D: int, page_size: int, ctx_len,

@@ -145,6 +145,19 @@ sp_status run_attention(const Shape& s, const void* q, const void* k, const void
   return SP_OK;
 }
 
+// Arguments shared by the layout calls, for n_layers layers whose policies are [n_layers][Hkv].
+sp_status check_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                       int32_t Hkv, const sp_head_policy* pol, int32_t page_size) {
+  if (n_layers < 1 || pol == nullptr) return SP_ERR_INVALID_ARG;
+  sp_status st = check_page_size(page_size);
+  if (st != SP_OK) return st;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    st = check_lengths_policy(B, ctx_len, q_len, Hkv, pol + size_t(l) * Hkv);
+    if (st != SP_OK) return st;
+  }
+  return SP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -165,30 +178,41 @@ const char* segpaged_status_string(int status) {
 sp_status segpaged_plan_pages(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
                               int32_t Hkv, const sp_head_policy* pol, int32_t page_size,
                               int64_t* n_pages_needed) {
+  return segpaged_plan_pages_layers(1, B, ctx_len, q_len, Hkv, pol, page_size, n_pages_needed);
+}
+
+sp_status segpaged_plan_pages_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len,
+                                     const int32_t* q_len, int32_t Hkv,
+                                     const sp_head_policy* pol, int32_t page_size,
+                                     int64_t* n_pages_needed) {
   if (n_pages_needed == nullptr) return SP_ERR_INVALID_ARG;
-  sp_status st = check_page_size(page_size);
-  if (st != SP_OK) return st;
-  st = check_lengths_policy(B, ctx_len, q_len, Hkv, pol);
+  sp_status st = check_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size);
   if (st != SP_OK) return st;
   Layout lay;
-  st = make_layout(B, ctx_len, q_len, Hkv, pol, page_size, &lay);
+  st = make_layout_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size, &lay);
   if (st != SP_OK) return st;
   *n_pages_needed = lay.n_virt;
   return SP_OK;
 }
 
 sp_status segpaged_layout_tables(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
-                                int32_t Hkv, const sp_head_policy* pol, int32_t page_size,
-                                int32_t* seg_table, int32_t* kv_len) {
+                                 int32_t Hkv, const sp_head_policy* pol, int32_t page_size,
+                                 int32_t* seg_table, int32_t* kv_len) {
+  return segpaged_layout_tables_layers(1, B, ctx_len, q_len, Hkv, pol, page_size, seg_table,
+                                       kv_len);
+}
+
+sp_status segpaged_layout_tables_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len,
+                                        const int32_t* q_len, int32_t Hkv,
+                                        const sp_head_policy* pol, int32_t page_size,
+                                        int32_t* seg_table, int32_t* kv_len) {
   if (seg_table == nullptr || kv_len == nullptr) return SP_ERR_INVALID_ARG;
-  sp_status st = check_page_size(page_size);
-  if (st != SP_OK) return st;
-  st = check_lengths_policy(B, ctx_len, q_len, Hkv, pol);
+  sp_status st = check_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size);
   if (st != SP_OK) return st;
   Layout lay;
-  st = make_layout(B, ctx_len, q_len, Hkv, pol, page_size, &lay);
+  st = make_layout_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size, &lay);
   if (st != SP_OK) return st;
-  layout_tables(lay, B, Hkv, seg_table, kv_len);
+  layout_tables(lay, n_layers * B * Hkv, seg_table, kv_len);
   return SP_OK;
 }
 
@@ -197,15 +221,28 @@ sp_status segpaged_build(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int3
                          const void* k_dense, const void* v_dense, const int32_t* free_pages,
                          int64_t n_free, int64_t n_phys, void* k_pool, void* v_pool,
                          int32_t* seg_table, int32_t* kv_len, int32_t* v2p, hipStream_t stream) {
+  return segpaged_build_layers(dtype, 1, B, Hkv, D, page_size, ctx_len, q_len, pol, k_dense,
+                               v_dense, free_pages, n_free, n_phys, k_pool, v_pool, seg_table,
+                               kv_len, v2p, stream);
+}
+
+sp_status segpaged_build_layers(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv,
+                                int32_t D, int32_t page_size, const int32_t* ctx_len,
+                                const int32_t* q_len, const sp_head_policy* pol,
+                                const void* k_dense, const void* v_dense,
+                                const int32_t* free_pages, int64_t n_free, int64_t n_phys,
+                                void* k_pool, void* v_pool, int32_t* seg_table, int32_t* kv_len,
+                                int32_t* v2p, hipStream_t stream) {
   sp_status st = check_dtype_dim(dtype, D);
   if (st != SP_OK) return st;
-  st = check_page_size(page_size);
-  if (st != SP_OK) return st;
-  st = check_lengths_policy(B, ctx_len, q_len, Hkv, pol);
+  st = check_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size);
   if (st != SP_OK) return st;
   if (n_free < 0 || n_phys < 0) return SP_ERR_INVALID_ARG;
+  int64_t t_total = 0;
+  for (int32_t b = 0; b < B; ++b) t_total += ctx_len[b];
+  if (int64_t(n_layers) * t_total > 0x7fffffffLL) return SP_ERR_UNSUPPORTED;  // int32 rows
   Layout lay;
-  st = make_layout(B, ctx_len, q_len, Hkv, pol, page_size, &lay);
+  st = make_layout_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size, &lay);
   if (st != SP_OK) return st;
   if (B == 0) return SP_OK;
   if (seg_table == nullptr || kv_len == nullptr) return SP_ERR_INVALID_ARG;
@@ -225,10 +262,11 @@ sp_status segpaged_build(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int3
   // Tables: seg_table, kv_len and v2p. When the caller placed them back to back in one
   // allocation they go up in a single host-to-device copy (each copy from pageable memory
   // costs tens of microseconds of fixed overhead), else in three.
-  const size_t n_tab = size_t(B) * Hkv * 8, n_kl = size_t(B) * Hkv;
+  const size_t n_heads = size_t(n_layers) * B * Hkv;
+  const size_t n_tab = n_heads * 8, n_kl = n_heads;
   const bool adjacent = kv_len == seg_table + n_tab && (n_virt == 0 || v2p == kv_len + n_kl);
   std::vector<int32_t> host(n_tab + n_kl + (adjacent ? size_t(n_virt) : 0));
-  layout_tables(lay, B, Hkv, host.data(), host.data() + n_tab);
+  layout_tables(lay, int32_t(n_heads), host.data(), host.data() + n_tab);
   if (adjacent) {
     if (n_virt > 0) std::memcpy(host.data() + n_tab + n_kl, free_pages, size_t(n_virt) * 4);
     if (hipMemcpyAsync(seg_table, host.data(), host.size() * 4, hipMemcpyHostToDevice,
@@ -246,7 +284,7 @@ sp_status segpaged_build(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int3
   }
   if (hipStreamSynchronize(stream) != hipSuccess) return SP_ERR_HIP;
 
-  // Scatter: one launch per run of at most kMaxBuildSegs non-empty segments.
+  // Scatter: one launch per run of at most kMaxBuildSegs non-empty segments, over all layers.
   BuildParams bp;
   std::memset(&bp, 0, sizeof(bp));
   bp.k = k_dense;
@@ -256,7 +294,6 @@ sp_status segpaged_build(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int3
   bp.v2p = v2p;
   bp.Hkv = Hkv;
   bp.P = page_size;
-  int64_t row0 = 0;
   auto flush = [&]() -> sp_status {
     if (bp.nseg == 0) return SP_OK;
     if (launch_build(dtype, D, bp, stream) != hipSuccess) return SP_ERR_HIP;
@@ -264,26 +301,29 @@ sp_status segpaged_build(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int3
     bp.nchunks = 0;
     return SP_OK;
   };
-  for (int32_t b = 0; b < B; ++b) {
-    for (int32_t h = 0; h < Hkv; ++h) {
-      const HeadLayout& hl = lay.heads[size_t(b) * Hkv + h];
-      for (int s = 0; s < hl.nseg; ++s) {
-        const Segment& sg = hl.seg[s];
-        if (sg.ntok == 0) continue;
-        if (bp.nseg == kMaxBuildSegs) {
-          st = flush();
-          if (st != SP_OK) return st;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    int64_t row0 = int64_t(l) * t_total;  // dense K/V of layer l start at row l * sum(ctx_len)
+    for (int32_t b = 0; b < B; ++b) {
+      for (int32_t h = 0; h < Hkv; ++h) {
+        const HeadLayout& hl = lay.heads[(size_t(l) * B + b) * Hkv + h];
+        for (int s = 0; s < hl.nseg; ++s) {
+          const Segment& sg = hl.seg[s];
+          if (sg.ntok == 0) continue;
+          if (bp.nseg == kMaxBuildSegs) {
+            st = flush();
+            if (st != SP_OK) return st;
+          }
+          BuildSeg& e = bp.seg[bp.nseg++];
+          e.chunk0 = bp.nchunks;
+          e.src_row0 = int32_t(row0 + sg.pos);
+          e.vstart = sg.vstart;
+          e.ntok = sg.ntok;
+          e.h = h;
+          bp.nchunks += (sg.ntok + kChunk - 1) / kChunk;
         }
-        BuildSeg& e = bp.seg[bp.nseg++];
-        e.chunk0 = bp.nchunks;
-        e.src_row0 = int32_t(row0 + sg.pos);
-        e.vstart = sg.vstart;
-        e.ntok = sg.ntok;
-        e.h = h;
-        bp.nchunks += (sg.ntok + kChunk - 1) / kChunk;
       }
+      row0 += ctx_len[b];
     }
-    row0 += ctx_len[b];
   }
   return flush();
 }

@@ -120,27 +120,35 @@ int head_segments(const sp_head_policy& pol_in, int32_t L, int32_t q, int32_t ou
 
 sp_status make_layout(int32_t B, const int32_t* ctx_len, const int32_t* q_len, int32_t Hkv,
                       const sp_head_policy* pol, int32_t P, Layout* out) {
-  out->heads.assign(size_t(B) * Hkv, HeadLayout{});
+  return make_layout_layers(1, B, ctx_len, q_len, Hkv, pol, P, out);
+}
+
+sp_status make_layout_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len,
+                             const int32_t* q_len, int32_t Hkv, const sp_head_policy* pol,
+                             int32_t P, Layout* out) {
+  out->heads.assign(size_t(n_layers) * B * Hkv, HeadLayout{});
   int64_t v = 0;
   for (int32_t b = 0; b < B; ++b) {
-    for (int32_t h = 0; h < Hkv; ++h) {
-      HeadLayout& hl = out->heads[size_t(b) * Hkv + h];
-      int32_t pos[2] = {0, 0}, ntok[2] = {0, 0};
-      hl.nseg = head_segments(pol[h], ctx_len[b], q_len[b], pos, ntok);
-      hl.kv_len = 0;
-      for (int s = 0; s < 2; ++s) {
-        Segment& sg = hl.seg[s];
-        if (s < hl.nseg) {
-          sg.pos = pos[s];
-          sg.ntok = ntok[s];
-          sg.vstart = int32_t(v);
-          sg.npages = int32_t(ceil_div(ntok[s], P));
-          v += sg.npages;
-          hl.kv_len += ntok[s];
-        } else {
-          sg = Segment{0, 0, int32_t(v), 0};
+    for (int32_t l = 0; l < n_layers; ++l) {
+      for (int32_t h = 0; h < Hkv; ++h) {
+        HeadLayout& hl = out->heads[(size_t(l) * B + b) * Hkv + h];
+        int32_t pos[2] = {0, 0}, ntok[2] = {0, 0};
+        hl.nseg = head_segments(pol[size_t(l) * Hkv + h], ctx_len[b], q_len[b], pos, ntok);
+        hl.kv_len = 0;
+        for (int s = 0; s < 2; ++s) {
+          Segment& sg = hl.seg[s];
+          if (s < hl.nseg) {
+            sg.pos = pos[s];
+            sg.ntok = ntok[s];
+            sg.vstart = int32_t(v);
+            sg.npages = int32_t(ceil_div(ntok[s], P));
+            v += sg.npages;
+            hl.kv_len += ntok[s];
+          } else {
+            sg = Segment{0, 0, int32_t(v), 0};
+          }
+          if (v > kInt32Max) return SP_ERR_UNSUPPORTED;
         }
-        if (v > kInt32Max) return SP_ERR_UNSUPPORTED;
       }
     }
   }
@@ -148,9 +156,9 @@ sp_status make_layout(int32_t B, const int32_t* ctx_len, const int32_t* q_len, i
   return SP_OK;
 }
 
-void layout_tables(const Layout& lay, int32_t B, int32_t Hkv, int32_t* seg_table,
+void layout_tables(const Layout& lay, int32_t n_heads_total, int32_t* seg_table,
                    int32_t* kv_len) {
-  for (int32_t i = 0; i < B * Hkv; ++i) {
+  for (int32_t i = 0; i < n_heads_total; ++i) {
     const HeadLayout& hl = lay.heads[i];
     for (int s = 0; s < 2; ++s) {
       int32_t* e = seg_table + (size_t(i) * 2 + s) * 4;

@@ -22,7 +22,9 @@ struct HeadLayout {
   int32_t kv_len;
 };
 
-// Page layout of one batch: heads[b * Hkv + h].
+// Page layout of one batch over n_layers layers: heads[(layer * B + b) * Hkv + h] (layer-major,
+// so each layer's tables are contiguous); virtual pages are numbered in (request, layer, head,
+// segment) order.
 struct Layout {
   std::vector<HeadLayout> heads;
   int64_t n_virt = 0;
@@ -53,9 +55,14 @@ int head_segments(const sp_head_policy& pol, int32_t L, int32_t q, int32_t out_p
 
 sp_status make_layout(int32_t B, const int32_t* ctx_len, const int32_t* q_len, int32_t Hkv,
                       const sp_head_policy* pol, int32_t P, Layout* out);
+// The same for n_layers layers sharing one page pool; pol is [n_layers][Hkv].
+sp_status make_layout_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len,
+                             const int32_t* q_len, int32_t Hkv, const sp_head_policy* pol,
+                             int32_t P, Layout* out);
 
 // Fills seg_table [B][Hkv][2][4] and kv_len [B][Hkv] from a layout.
-void layout_tables(const Layout& lay, int32_t B, int32_t Hkv, int32_t* seg_table,
+// seg_table [n_layers][B][Hkv][2][4] and kv_len [n_layers][B][Hkv] of a layout.
+void layout_tables(const Layout& lay, int32_t n_heads_total, int32_t* seg_table,
                    int32_t* kv_len);
 
 uint64_t shape_signature(const Shape& s, int32_t slots_prefill, int32_t slots_decode);

@@ -90,6 +90,76 @@ class SegPagedLayer:
         return B.segpaged_attention_check(self.workspace, stream)
 
 
+class SegPagedLayers:
+    """Several layers of one batch in ONE page pool, built by one call (page "RedKnot
+    SegPagedAttention runtime design", section 3: the page table is keyed by (layer, head,
+    segment)). Dense K/V come stacked as [n_layers, T, Hkv, D]; layer l is attended through its
+    own slice of the tables, its own work list and the shared pools and v2p."""
+
+    def __init__(self, dtype, n_layers: int, Hq: int, Hkv: int, D: int, page_size: int, ctx_len,
+                 q_len, policies, device: str = "cuda"):
+        self.dtype = _dt(dtype)
+        self.n_layers = int(n_layers)
+        self.Hq, self.Hkv, self.D, self.P = int(Hq), int(Hkv), int(D), int(page_size)
+        self.ctx_len = np.asarray(ctx_len, dtype=np.int32)
+        self.q_len = np.asarray(q_len, dtype=np.int32)
+        self.policies = np.asarray(policies, dtype=np.int32).reshape(self.n_layers, self.Hkv, 3)
+        self.device = device
+        self.n_virt = B.segpaged_plan_pages_layers(self.ctx_len, self.q_len, self.policies,
+                                                   self.P)
+        self.k_pool = self.v_pool = None
+        self.seg_table = self.kv_len = self.v2p = None
+        self.workspaces = [None] * self.n_layers
+        self.n_phys = 0
+
+    def build(self, k_dense: torch.Tensor, v_dense: torch.Tensor, free_pages,
+              n_phys: int | None = None, stream=None) -> None:
+        """Allocate the shared pool and the tables and fill them from all layers' dense K/V."""
+        self.n_phys = int(n_phys if n_phys is not None else max(self.n_virt, 1))
+        t = _TORCH[self.dtype]
+        self.k_pool = torch.empty((max(self.n_phys, 1), self.P, self.D), dtype=t,
+                                  device=self.device)
+        self.v_pool = torch.empty_like(self.k_pool)
+        Bn = max(len(self.ctx_len), 1)
+        n_tab, n_kl = self.n_layers * Bn * self.Hkv * 8, self.n_layers * Bn * self.Hkv
+        tables = torch.zeros((n_tab + n_kl + max(self.n_virt, 1),), dtype=torch.int32,
+                             device=self.device)
+        self.seg_table = tables[:n_tab].view(self.n_layers, Bn, self.Hkv, 2, 4)
+        self.kv_len = tables[n_tab:n_tab + n_kl].view(self.n_layers, Bn, self.Hkv)
+        self.v2p = tables[n_tab + n_kl:]
+        self.rebuild(k_dense, v_dense, free_pages, stream)
+
+    def rebuild(self, k_dense: torch.Tensor, v_dense: torch.Tensor, free_pages,
+                stream=None) -> None:
+        """Refill the already allocated pool and tables (no allocation)."""
+        B.segpaged_build_layers(self.dtype, self.D, self.P, self.ctx_len, self.q_len,
+                                self.policies, k_dense, v_dense,
+                                np.asarray(free_pages, dtype=np.int32), self.n_phys,
+                                self.k_pool, self.v_pool, self.seg_table, self.kv_len, self.v2p,
+                                stream)
+
+    def attention(self, layer: int, q: torch.Tensor, scale: float,
+                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        pol = self.policies[layer]
+        if self.workspaces[layer] is None:
+            n = B.segpaged_attention_workspace_size(self.dtype, self.Hq, self.Hkv, self.D,
+                                                    self.P, self.ctx_len, self.q_len, pol)
+            ws = torch.zeros((n,), dtype=torch.uint8, device=self.device)
+            B.segpaged_attention_plan(self.dtype, self.Hq, self.Hkv, self.D, self.P,
+                                      self.ctx_len, self.q_len, pol, ws, stream)
+            self.workspaces[layer] = ws
+        if out is None:
+            out = torch.empty_like(q)
+        B.segpaged_attention(self.dtype, self.Hq, self.Hkv, self.D, self.P, self.ctx_len,
+                             self.q_len, pol, q, self.k_pool, self.v_pool, self.n_phys,
+                             self.seg_table[layer], self.kv_len[layer], self.v2p, scale, out,
+                             self.workspaces[layer], stream=stream)
+        return out
+
+    def check(self, layer: int, stream=None) -> int:
+        return B.segpaged_attention_check(self.workspaces[layer], stream)
+
+
 class DenseMaskLayer:
     def __init__(self, dtype, Hq: int, Hkv: int, D: int, ctx_len, q_len, policy,
                  device: str = "cuda"):

@@ -131,6 +131,36 @@ sp_status segpaged_build(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int3
                          void* k_pool, void* v_pool,
                          int32_t* seg_table, int32_t* kv_len, int32_t* v2p, hipStream_t stream);
 
+/* The layout of n_layers layers of one batch in ONE page pool and one v2p (page "RedKnot
+ * SegPagedAttention runtime design", section 3: the page table is keyed by (layer, head,
+ * segment)). Virtual pages are numbered in (request, layer, head, segment) order; each layer's
+ * segments follow the single-layer rules with that layer's policies. n_layers = 1 gives exactly
+ * segpaged_plan_pages / segpaged_layout_tables / segpaged_build.
+ *   pol              : host [n_layers][Hkv]
+ *   k_dense, v_dense : device [n_layers][sum(ctx_len)][Hkv][D] (layers stacked)
+ *   seg_table        : int32 [n_layers][B][Hkv][2][4]   (device for build, host for tables)
+ *   kv_len           : int32 [n_layers][B][Hkv]
+ *   v2p              : device int32 [n_virt] (n_virt from segpaged_plan_pages_layers)
+ * Layer l is then served by segpaged_attention with pol + l*Hkv, seg_table + l*B*Hkv*8,
+ * kv_len + l*B*Hkv and the shared v2p and pools. Errors as the single-layer calls, plus
+ * SP_ERR_INVALID_ARG for n_layers < 1 and SP_ERR_UNSUPPORTED when n_layers * sum(ctx_len)
+ * exceeds 2^31 - 1 rows. */
+sp_status segpaged_plan_pages_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len,
+                                     const int32_t* q_len, int32_t Hkv,
+                                     const sp_head_policy* pol, int32_t page_size,
+                                     int64_t* n_pages_needed);
+sp_status segpaged_layout_tables_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len,
+                                        const int32_t* q_len, int32_t Hkv,
+                                        const sp_head_policy* pol, int32_t page_size,
+                                        int32_t* seg_table, int32_t* kv_len);
+sp_status segpaged_build_layers(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv,
+                                int32_t D, int32_t page_size, const int32_t* ctx_len,
+                                const int32_t* q_len, const sp_head_policy* pol,
+                                const void* k_dense, const void* v_dense,
+                                const int32_t* free_pages, int64_t n_free, int64_t n_phys,
+                                void* k_pool, void* v_pool, int32_t* seg_table, int32_t* kv_len,
+                                int32_t* v2p, hipStream_t stream);
+
 /* Bytes of device workspace segpaged_attention needs for these arguments (host only). The
  * workspace holds the work list (one item per (request, KV head, query block, KV split),
  * per-XCD queues and counters) and the fp32 partial results of KV-split items. */

@@ -28,4 +28,4 @@ example). Nothing here is "parity unpinned".
 
 from .attention import GLOBAL, LOCAL, attention, attention_rows, to_f64, visible  # noqa: F401
 from .plan import (LOCAL_ADAPTIVE, gather_positions, head_policy, plan_tables,  # noqa: F401
-                   segments)
+                   plan_tables_layers, segments)

@@ -23,6 +23,9 @@ Readings taken where the pages are silent (one layer per call):
 * An unused segment slot reads (pos_start 0, n_tok 0, vpage_start = running total, n_pages 0).
 * v2p[v] = free_pages[v]: physical pages are taken from the caller's free list in order.
 * kv_len[b, h] = total stored tokens of the head.
+* Several layers in one pool (same page, section 3: the page table is keyed by (layer, head,
+  segment)): each layer's heads follow the rules above with that layer's policies, and virtual
+  pages are handed out in (request, layer, head, segment) order; tables are stored per layer.
 * An adaptive LOCAL head (page "RedKnot head classification", the passage on windows that
   scale with each request's context length, whose example is half the context) is a LOCAL
   head whose window for a request of context length L is max(1, L // d), d being its
@@ -87,6 +90,33 @@ def plan_tables(ctx_len, q_len, policy, P: int):
                 else:
                     seg_table[b, h, s] = (0, 0, v, 0)
             kv_len[b, h] = total
+    return seg_table, kv_len, v
+
+
+def plan_tables_layers(ctx_len, q_len, policies, P: int):
+    """Several layers in one pool: policies [n_layers][Hkv][3]. Returns (seg_table int32
+    [n_layers, B, Hkv, 2, 4], kv_len int32 [n_layers, B, Hkv], n_virt)."""
+    policies = np.asarray(policies, dtype=np.int64)
+    n_layers, Hkv = policies.shape[0], policies.shape[1]
+    B = len(ctx_len)
+    seg_table = np.zeros((n_layers, B, Hkv, 2, 4), dtype=np.int32)
+    kv_len = np.zeros((n_layers, B, Hkv), dtype=np.int32)
+    v = 0
+    for b in range(B):  # virtual pages: request, then layer, then head, then segment
+        L, q = int(ctx_len[b]), int(q_len[b])
+        for layer in range(n_layers):
+            for h in range(Hkv):
+                kind, sink, window = head_policy(*(int(x) for x in policies[layer, h]), L)
+                segs = segments(kind, sink, window, L, q)
+                for s in range(2):
+                    if s < len(segs):
+                        pos, n = segs[s]
+                        npg = -(-n // P)
+                        seg_table[layer, b, h, s] = (pos, n, v, npg)
+                        v += npg
+                        kv_len[layer, b, h] += n
+                    else:
+                        seg_table[layer, b, h, s] = (0, 0, v, 0)
     return seg_table, kv_len, v
 
 

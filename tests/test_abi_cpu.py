@@ -135,3 +135,37 @@ def test_build_validates_free_list_before_touching_memory():
     assert lib.segpaged_build(0, 1, 1, 96, 16, binding._ptr(c), binding._ptr(ql),
                               binding._ptr(p), fake, fake, None, 0, 0, fake, fake, fake, fake,
                               fake, None) == binding.SP_ERR_UNSUPPORTED
+
+
+def test_layers_layout_tables_match_oracle():
+    # The multi-layer layout (one pool, pages numbered by request, layer, head, segment) from
+    # the library's host code, against the oracle's tables.
+    from oracle import plan_tables_layers
+    rng = np.random.default_rng(21)
+    for _ in range(60):
+        n_layers, B, Hkv = int(rng.integers(1, 5)), int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        P = int(rng.choice([16, 64, 256]))
+        ctx = rng.integers(0, 900, size=B)
+        q = np.array([rng.integers(0, c + 1) for c in ctx])
+        pol = np.array([[(int(rng.integers(0, 3)), int(rng.integers(0, 30)),
+                          int(rng.integers(1, 5)) if rng.random() < 0.3 else int(rng.integers(1, 500)))
+                         for _ in range(Hkv)] for _ in range(n_layers)], dtype=np.int32)
+        pol[pol[:, :, 0] == 2, 2] = np.minimum(pol[pol[:, :, 0] == 2, 2], 8)  # adaptive: divisor
+        seg, kvl = sp.segpaged_layout_tables_layers(ctx, q, pol, P)
+        seg_o, kvl_o, n_virt = plan_tables_layers(ctx, q, pol, P)
+        np.testing.assert_array_equal(seg, seg_o)
+        np.testing.assert_array_equal(kvl, kvl_o)
+        assert sp.segpaged_plan_pages_layers(ctx, q, pol, P) == n_virt
+
+
+def test_layers_invalid_arguments():
+    lib = binding.lib()
+    c = np.array([10], np.int32)
+    q = np.array([1], np.int32)
+    pol = np.array([(1, 4, 64)], np.int32)
+    out = binding._i64(0)
+    assert lib.segpaged_plan_pages_layers(0, 1, binding._ptr(c), binding._ptr(q), 1,
+                                          binding._ptr(pol), 16,
+                                          binding.ctypes.byref(out)) == binding.SP_ERR_INVALID_ARG
+    with pytest.raises(sp.SegPagedError):  # second layer's policy invalid
+        sp.segpaged_plan_pages_layers([10], [1], [[(1, 4, 64)], [(1, 4, 0)]], 16)

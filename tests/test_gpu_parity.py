@@ -328,3 +328,33 @@ def test_random_shapes_against_oracle(args):
     np.testing.assert_array_equal(layer.seg_table.cpu().numpy()[:c.B], seg_o)
     np.testing.assert_array_equal(layer.kv_len.cpu().numpy()[:c.B], kvl_o)
     assert_parity(to_f64(out), _oracle(c), c, "random")
+
+
+def test_layers_share_one_pool():
+    # Three layers of one batch (different policies, one adaptive) built by one call into one
+    # pool: each layer's tables equal the oracle's multi-layer tables, its stored rows equal
+    # its dense rows bit for bit, and attention on each layer matches the oracle.
+    from head_aware_paged_segpaged_amd import SegPagedLayers
+    shapes = dict(dtype="bf16", Hq=8, Hkv=2, D=128, P=64, ctx_len=[700, 260], q_len=[90, 1])
+    policies = [[(G_, 0, 1), (L_, 4, 100)], [(L_, 0, 33), (G_, 0, 1)], [(A_, 4, 3), (L_, 2, 500)]]
+    cases = [custom_case(40 + i, policy=pol, **shapes) for i, pol in enumerate(policies)]
+    print("case layers", len(cases), flush=True)
+    c0 = cases[0]
+    stack = lambda xs: torch.stack([to_device(x, c0.dtype) for x in xs])
+    k_all, v_all = stack([c.k for c in cases]), stack([c.v for c in cases])
+    m = SegPagedLayers(c0.dtype, len(cases), c0.Hq, c0.Hkv, c0.D, c0.P, c0.ctx_len, c0.q_len,
+                       policies, DEV)
+    n_phys = m.n_virt + 5
+    fl = np.random.default_rng(8).permutation(n_phys).astype(np.int32)
+    m.build(k_all, v_all, fl, n_phys=n_phys)
+    torch.cuda.synchronize()
+    seg_o, kvl_o, n_virt = oracle.plan_tables_layers(c0.ctx_len, c0.q_len, policies, c0.P)
+    assert m.n_virt == n_virt
+    np.testing.assert_array_equal(m.seg_table.cpu().numpy(), seg_o)
+    np.testing.assert_array_equal(m.kv_len.cpu().numpy(), kvl_o)
+    for layer, c in enumerate(cases):
+        _check_pool(c, seg_o[layer], fl, m.k_pool, m.v_pool)
+        out = m.attention(layer, to_device(c.q, c.dtype), c.scale)
+        torch.cuda.synchronize()
+        assert m.check(layer) == 0
+        assert_parity(to_f64(out), _oracle(c), c, "layer %d" % layer)

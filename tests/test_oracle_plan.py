@@ -154,3 +154,44 @@ def test_adaptive_window_divisor_one_stores_like_global():
         g = plan_tables(L, q, [(GLOBAL, 0, 1)], 32)
         np.testing.assert_array_equal(a[0], g[0])
         np.testing.assert_array_equal(a[1], g[1])
+
+
+def test_layers_worked_example():
+    # Two layers, two requests, one KV head, pages of 16 (virtual pages in request, layer,
+    # head, segment order). Layer 0: GLOBAL. Layer 1: LOCAL sink 2, window 20.
+    #   request 0, L = 50, q = 10: layer 0 (0, 50) -> 4 pages [0, 4);
+    #     layer 1: R0 = 50 - 10 - 20 + 1 = 21 -> (0, 2) 1 page [4], (21, 29) 2 pages [5, 7).
+    #   request 1, L = 16, q = 16: layer 0 (0, 16) -> 1 page [7];
+    #     layer 1: R0 = max(0, 16 - 16 - 20 + 1) = 0 <= 2 -> one segment (0, 16), 1 page [8].
+    from oracle import plan_tables_layers
+    pol = [[(GLOBAL, 0, 1)], [(LOCAL, 2, 20)]]
+    seg, kv_len, n_virt = plan_tables_layers([50, 16], [10, 16], pol, 16)
+    np.testing.assert_array_equal(seg[0, 0, 0], [[0, 50, 0, 4], [0, 0, 4, 0]])
+    np.testing.assert_array_equal(seg[1, 0, 0], [[0, 2, 4, 1], [21, 29, 5, 2]])
+    np.testing.assert_array_equal(seg[0, 1, 0], [[0, 16, 7, 1], [0, 0, 8, 0]])
+    np.testing.assert_array_equal(seg[1, 1, 0], [[0, 16, 8, 1], [0, 0, 9, 0]])
+    np.testing.assert_array_equal(kv_len, [[[50], [16]], [[31], [16]]])
+    assert n_virt == 9
+
+
+def test_layers_match_single_layer_tables_up_to_page_numbering():
+    # Each layer stores what a one-layer layout with its policies stores; only the virtual
+    # page numbers move, and the totals add up.
+    from oracle import plan_tables_layers
+    rng = np.random.default_rng(11)
+    for _ in range(30):
+        B, Hkv, n_layers = int(rng.integers(1, 4)), int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        ctx = rng.integers(0, 400, B)
+        q = np.array([int(rng.integers(0, x + 1)) for x in ctx])
+        pol = [[(int(rng.integers(0, 3)), int(rng.integers(0, 9)), int(rng.integers(1, 6)) * 17)
+                for _ in range(Hkv)] for _ in range(n_layers)]
+        seg, kvl, n_virt = plan_tables_layers(ctx, q, pol, 32)
+        total = 0
+        for layer in range(n_layers):
+            s1, k1, n1 = plan_tables(ctx, q, pol[layer], 32)
+            np.testing.assert_array_equal(seg[layer][..., [0, 1, 3]], s1[..., [0, 1, 3]])
+            np.testing.assert_array_equal(kvl[layer], k1)
+            total += n1
+        assert n_virt == total
+        if n_layers == 1:
+            np.testing.assert_array_equal(seg[0], plan_tables(ctx, q, pol[0], 32)[0])
