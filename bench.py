@@ -159,6 +159,10 @@ def main() -> int:
                     help="no GPU run: turn two rocprofv3 --pmc runs of this workload "
                          "(FETCH_SIZE, then WRITE_SIZE, each with --copy-calibration) into "
                          "HBM bytes per launch of its main kernel in profiles/traffic.json")
+    ap.add_argument("--build-layers", type=int, default=0, metavar="N",
+                    help="also time one build of N layers of this workload's shape into one "
+                         "shared page pool (layer l's KV-head policies are the workload's "
+                         "rolled by l heads); reported as build_layers; 0 skips it")
     ap.add_argument("--gemm-reference", action="store_true",
                     help="only time torch's bf16 GEMM (hipBLASLt) at 4096^3..16384^3: what a "
                          "vendor-tuned dense contraction reaches on this GPU, for context")
@@ -174,7 +178,8 @@ def main() -> int:
 
     import torch
 
-    from head_aware_paged_segpaged_amd import DenseMaskLayer, HipEvent, SegPagedLayer
+    from head_aware_paged_segpaged_amd import (DenseMaskLayer, HipEvent, SegPagedLayer,
+                                               SegPagedLayers)
     from workloads import config_case, free_list
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -371,6 +376,10 @@ def main() -> int:
                                    % (cpu_nrows, len(sample), case.B * case.Hq, blas_name(),
                                       cpu_s, os.cpu_count() or 0)},
     }
+    if args.build_layers > 0:
+        del layer
+        line["build_layers"] = build_layers_leg(args.build_layers, case, k, v, evict, stream,
+                                                SegPagedLayers, HipEvent, build_ms)
     print(json.dumps(line), flush=True)
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -380,6 +389,47 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
     return 0
+
+
+def build_layers_leg(n_layers, case, k, v, evict, stream, layers_cls, event_cls,
+                     one_layer_ms) -> dict:
+    """Median time of building ``n_layers`` layers of the workload's shape in one call into one
+    shared pool: the stacked dense K/V are the workload's layer repeated (values do not change
+    the build's work), the policies differ per layer."""
+    import torch
+    pol = np.stack([np.roll(case.policy, l, axis=0) for l in range(n_layers)])
+    layers = layers_cls(case.dtype, n_layers, case.Hq, case.Hkv, case.D, case.P, case.ctx_len,
+                        case.q_len, pol, k.device)
+    elem = k.element_size()
+    need = 2.0 * n_layers * k.numel() * elem + 2.0 * layers.n_virt * case.P * case.D * elem
+    free, _ = torch.cuda.mem_get_info()
+    if need > 0.8 * free:
+        return {"layers": n_layers, "skipped": "needs %.1f GiB of %.1f GiB free"
+                % (need / 2 ** 30, free / 2 ** 30)}
+    kd = k.unsqueeze(0).expand(n_layers, *k.shape).contiguous()
+    vd = v.unsqueeze(0).expand(n_layers, *v.shape).contiguous()
+    fl = np.random.default_rng(case.seed).permutation(max(layers.n_virt, 1)).astype(np.int32)
+    layers.build(kd, vd, fl)
+    walls, streams = [], []
+    for _ in range(BUILD_RUNS):
+        evict()
+        torch.cuda.synchronize()
+        b0, b1 = event_cls(), event_cls()
+        t0 = time.perf_counter()
+        b0.record(stream)
+        layers.rebuild(kd, vd, fl)
+        b1.record(stream)
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+        streams.append(b0.elapsed_ms(b1))
+    wall_s, ms = float(np.median(walls)), float(np.median(streams))
+    rows = float(layers.kv_len.sum().item())
+    nbytes = 2.0 * 2.0 * rows * case.D * elem  # read + write, K and V
+    return {"layers": n_layers, "pages": int(layers.n_virt), "runs": BUILD_RUNS,
+            "seconds": round(wall_s, 6), "stream_ms": round(ms, 4), "bytes": nbytes,
+            "gbps_wall": round(nbytes / wall_s / 1e9, 1),
+            "gbps_stream": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "vs_layers_times_one_layer_build": round(ms / (n_layers * one_layer_ms), 3)}
 
 
 def blas_name() -> str:
