@@ -19,6 +19,11 @@ What it computes, and from which passage of the RedKnot pages:
   virtual-to-physical map (page "RedKnot SegPagedAttention runtime design", section 3: one
   page table per (layer, head, segment) over contiguous virtual pages, a shared physical
   pool, LOCAL heads allocate only sink + recent pages).
+* ``append``: the growable page layout (each segment owns pages for a reserve of decode
+  tokens) and the decode-time append, where a LOCAL head's recent segment is a ring of whole
+  pages whose oldest page is recycled once it falls out of the window (page "RedKnot
+  SegPagedAttention runtime design", section 3: LOCAL storage does not grow with the context;
+  the product overview page, section 3.2: idle pages are reclaimed).
 * ``brute``: pure-Python float loops on tiny inputs, used to pin ``attention``.
 
 Parity status: every function here is pinned by tests under ``tests/test_oracle_*.py``
@@ -29,3 +34,4 @@ example). Nothing here is "parity unpinned".
 from .attention import GLOBAL, LOCAL, attention, attention_rows, to_f64, visible  # noqa: F401
 from .plan import (LOCAL_ADAPTIVE, gather_positions, head_policy, plan_tables,  # noqa: F401
                    plan_tables_layers, segments)
+from .append import append_step, grow_tables, owned_pages  # noqa: F401
