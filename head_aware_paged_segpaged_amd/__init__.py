@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     HipEvent,
     SegPagedError,
     lib,
+    SP_ERR_SEGMENT_FULL,
+    segpaged_append,
     segpaged_attention,
     segpaged_attention_check,
     segpaged_attention_plan,
@@ -21,14 +23,21 @@ from .binding import (  # noqa: F401
     segpaged_attention_profiled,
     segpaged_attention_workspace_size,
     segpaged_build,
+    segpaged_build_growable,
     segpaged_build_layers,
+    segpaged_decode,
+    segpaged_decode_plan,
+    segpaged_decode_workspace_size,
     segpaged_dense_mask_attention,
     segpaged_dense_mask_plan,
     segpaged_dense_mask_workspace_size,
     segpaged_layout_tables,
+    segpaged_layout_tables_growable,
     segpaged_layout_tables_layers,
     segpaged_plan_pages,
+    segpaged_plan_pages_growable,
     segpaged_plan_pages_layers,
     status_string,
 )
-from .runtime import DenseMaskLayer, SegPagedLayer, SegPagedLayers  # noqa: F401
+from .runtime import (DenseMaskLayer, SegPagedDecoder, SegPagedLayer,  # noqa: F401
+                      SegPagedLayers)

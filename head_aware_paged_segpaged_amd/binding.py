@@ -24,6 +24,7 @@ SP_ERR_POOL_TOO_SMALL = -3
 SP_ERR_WORKSPACE_TOO_SMALL = -4
 SP_ERR_HIP = -5
 SP_ERR_PLAN_MISMATCH = -6
+SP_ERR_SEGMENT_FULL = -7
 
 SP_BF16 = 0
 SP_F32 = 1
@@ -39,6 +40,13 @@ EXPORTED = [
     "segpaged_layout_tables_layers",
     "segpaged_build",
     "segpaged_build_layers",
+    "segpaged_plan_pages_growable",
+    "segpaged_layout_tables_growable",
+    "segpaged_build_growable",
+    "segpaged_append",
+    "segpaged_decode_workspace_size",
+    "segpaged_decode_plan",
+    "segpaged_decode",
     "segpaged_attention_workspace_size",
     "segpaged_attention_plan",
     "segpaged_attention",
@@ -74,6 +82,19 @@ _SIGS = {
                                      _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "segpaged_build": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                               _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "segpaged_plan_pages_growable": (_i32, [_i32, _vp, _vp, _vp, _i32, _vp, _i32,
+                                            ctypes.POINTER(_i64)]),
+    "segpaged_layout_tables_growable": (_i32, [_i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp]),
+    "segpaged_build_growable": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "segpaged_append": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                               _vp, _vp, _vp, _i64, _vp, _vp]),
+    "segpaged_decode_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                              ctypes.POINTER(_sz)]),
+    "segpaged_decode_plan": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
+                                    _vp]),
+    "segpaged_decode": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64,
+                               _vp, _vp, _vp, _f, _vp, _vp, _sz, _vp]),
     "segpaged_attention_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                                  _vp, ctypes.POINTER(_sz)]),
     "segpaged_attention_plan": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
@@ -228,6 +249,91 @@ def segpaged_build_layers(dtype, D: int, page_size: int, ctx_len, q_len, policy,
                                        _dev(v_pool, "v_pool"), _dev(seg_table, "seg_table"),
                                        _dev(kv_len, "kv_len"), _dev(v2p, "v2p"),
                                        _stream(stream)), "segpaged_build_layers")
+
+
+def segpaged_plan_pages_growable(ctx_len, q_len, reserve, policy, page_size: int) -> int:
+    c, q, r = _host_i32(ctx_len), _host_i32(q_len), _host_i32(reserve)
+    p = _host_i32(policy).reshape(-1, 3)
+    out = _i64(0)
+    _check(lib().segpaged_plan_pages_growable(len(c), _ptr(c), _ptr(q), _ptr(r), p.shape[0],
+                                              _ptr(p), page_size, ctypes.byref(out)),
+           "segpaged_plan_pages_growable")
+    return int(out.value)
+
+
+def segpaged_layout_tables_growable(ctx_len, q_len, reserve, policy, page_size: int):
+    c, q, r = _host_i32(ctx_len), _host_i32(q_len), _host_i32(reserve)
+    p = _host_i32(policy).reshape(-1, 3)
+    B, Hkv = len(c), p.shape[0]
+    seg = np.zeros((B, Hkv, 2, 4), dtype=np.int32)
+    kvl = np.zeros((B, Hkv), dtype=np.int32)
+    _check(lib().segpaged_layout_tables_growable(B, _ptr(c), _ptr(q), _ptr(r), Hkv, _ptr(p),
+                                                 page_size, seg.ctypes.data_as(_vp),
+                                                 kvl.ctypes.data_as(_vp)),
+           "segpaged_layout_tables_growable")
+    return seg, kvl
+
+
+def segpaged_build_growable(dtype, D: int, page_size: int, ctx_len, q_len, reserve, policy,
+                            k_dense, v_dense, free_pages, n_phys: int, k_pool, v_pool, seg_table,
+                            kv_len, v2p, stream=None) -> None:
+    c, q, r = _host_i32(ctx_len), _host_i32(q_len), _host_i32(reserve)
+    p, fl = _host_i32(policy).reshape(-1, 3), _host_i32(free_pages)
+    _check(lib().segpaged_build_growable(_dtype_code(dtype), len(c), p.shape[0], D, page_size,
+                                         _ptr(c), _ptr(q), _ptr(r), _ptr(p),
+                                         _dev(k_dense, "k_dense"), _dev(v_dense, "v_dense"),
+                                         _ptr(fl), fl.size, n_phys, _dev(k_pool, "k_pool"),
+                                         _dev(v_pool, "v_pool"), _dev(seg_table, "seg_table"),
+                                         _dev(kv_len, "kv_len"), _dev(v2p, "v2p"),
+                                         _stream(stream)), "segpaged_build_growable")
+
+
+def segpaged_append(dtype, D: int, page_size: int, policy, n_new, k_new, v_new, k_pool, v_pool,
+                    n_phys: int, seg_table, kv_len, v2p, error, stream=None) -> None:
+    """k_new, v_new: device [B][Hkv][D]; n_new: device int32 [B] or None; error: device int32."""
+    p = _host_i32(policy).reshape(-1, 3)
+    B = int(k_new.shape[0])
+    _check(lib().segpaged_append(_dtype_code(dtype), B, p.shape[0], D, page_size, _ptr(p),
+                                 _dev(n_new, "n_new"), _dev(k_new, "k_new"),
+                                 _dev(v_new, "v_new"), _dev(k_pool, "k_pool"),
+                                 _dev(v_pool, "v_pool"), int(n_phys),
+                                 _dev(seg_table, "seg_table"), _dev(kv_len, "kv_len"),
+                                 _dev(v2p, "v2p"), int(v2p.numel()), _dev(error, "error"),
+                                 _stream(stream)), "segpaged_append")
+
+
+def segpaged_decode_workspace_size(dtype, Hq: int, Hkv: int, D: int, page_size: int, ctx_hint,
+                                   policy) -> int:
+    c, p = _host_i32(ctx_hint), _host_i32(policy).reshape(-1, 3)
+    out = _sz(0)
+    _check(lib().segpaged_decode_workspace_size(_dtype_code(dtype), len(c), Hq, Hkv, D,
+                                                page_size, _ptr(c), _ptr(p), ctypes.byref(out)),
+           "segpaged_decode_workspace_size")
+    return int(out.value)
+
+
+def segpaged_decode_plan(dtype, Hq: int, Hkv: int, D: int, page_size: int, ctx_hint, policy,
+                         workspace, stream=None) -> None:
+    c, p = _host_i32(ctx_hint), _host_i32(policy).reshape(-1, 3)
+    _check(lib().segpaged_decode_plan(_dtype_code(dtype), len(c), Hq, Hkv, D, page_size, _ptr(c),
+                                      _ptr(p), _dev(workspace, "workspace"),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream)), "segpaged_decode_plan")
+
+
+def segpaged_decode(dtype, Hq: int, Hkv: int, D: int, page_size: int, policy, q, k_pool, v_pool,
+                    n_phys: int, seg_table, kv_len, v2p, scale: float, o, workspace,
+                    stream=None) -> None:
+    """q, o: device [B][Hq][D] (one decode query per request)."""
+    p = _host_i32(policy).reshape(-1, 3)
+    _check(lib().segpaged_decode(_dtype_code(dtype), int(q.shape[0]), Hq, Hkv, D, page_size,
+                                 _ptr(p), _dev(q, "q"), _dev(k_pool, "k_pool"),
+                                 _dev(v_pool, "v_pool"), int(n_phys),
+                                 _dev(seg_table, "seg_table"), _dev(kv_len, "kv_len"),
+                                 _dev(v2p, "v2p"), float(scale), _dev(o, "o"),
+                                 _dev(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "segpaged_decode")
 
 
 def segpaged_attention_workspace_size(dtype, Hq: int, Hkv: int, D: int, page_size: int, ctx_len,

@@ -158,92 +158,36 @@ sp_status check_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len, cons
   return SP_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* segpaged_status_string(int status) {
-  switch (status) {
-    case SP_OK: return "SP_OK";
-    case SP_ERR_INVALID_ARG: return "SP_ERR_INVALID_ARG: invalid argument";
-    case SP_ERR_UNSUPPORTED: return "SP_ERR_UNSUPPORTED: unsupported shape, dtype or size";
-    case SP_ERR_POOL_TOO_SMALL: return "SP_ERR_POOL_TOO_SMALL: free list shorter than needed";
-    case SP_ERR_WORKSPACE_TOO_SMALL: return "SP_ERR_WORKSPACE_TOO_SMALL: workspace too small";
-    case SP_ERR_HIP: return "SP_ERR_HIP: HIP runtime error";
-    case SP_ERR_PLAN_MISMATCH: return "SP_ERR_PLAN_MISMATCH: workspace planned for other arguments";
-    default: return "unknown status";
+// Checks and layout of n_layers layers; growable (single layer) when `reserve` is not null.
+sp_status layout_impl(int32_t n_layers, int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                      const int32_t* reserve, int32_t Hkv, const sp_head_policy* pol,
+                      int32_t page_size, Layout* lay) {
+  sp_status st = check_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size);
+  if (st != SP_OK) return st;
+  if (reserve != nullptr) {
+    if (n_layers != 1) return SP_ERR_INVALID_ARG;
+    st = check_growable(B, ctx_len, reserve, Hkv, pol);
+    if (st != SP_OK) return st;
   }
+  return make_layout_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size, reserve, lay);
 }
 
-sp_status segpaged_plan_pages(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
-                              int32_t Hkv, const sp_head_policy* pol, int32_t page_size,
-                              int64_t* n_pages_needed) {
-  return segpaged_plan_pages_layers(1, B, ctx_len, q_len, Hkv, pol, page_size, n_pages_needed);
-}
-
-sp_status segpaged_plan_pages_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len,
-                                     const int32_t* q_len, int32_t Hkv,
-                                     const sp_head_policy* pol, int32_t page_size,
-                                     int64_t* n_pages_needed) {
-  if (n_pages_needed == nullptr) return SP_ERR_INVALID_ARG;
-  sp_status st = check_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size);
-  if (st != SP_OK) return st;
-  Layout lay;
-  st = make_layout_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size, &lay);
-  if (st != SP_OK) return st;
-  *n_pages_needed = lay.n_virt;
-  return SP_OK;
-}
-
-sp_status segpaged_layout_tables(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
-                                 int32_t Hkv, const sp_head_policy* pol, int32_t page_size,
-                                 int32_t* seg_table, int32_t* kv_len) {
-  return segpaged_layout_tables_layers(1, B, ctx_len, q_len, Hkv, pol, page_size, seg_table,
-                                       kv_len);
-}
-
-sp_status segpaged_layout_tables_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len,
-                                        const int32_t* q_len, int32_t Hkv,
-                                        const sp_head_policy* pol, int32_t page_size,
-                                        int32_t* seg_table, int32_t* kv_len) {
-  if (seg_table == nullptr || kv_len == nullptr) return SP_ERR_INVALID_ARG;
-  sp_status st = check_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size);
-  if (st != SP_OK) return st;
-  Layout lay;
-  st = make_layout_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size, &lay);
-  if (st != SP_OK) return st;
-  layout_tables(lay, n_layers * B * Hkv, seg_table, kv_len);
-  return SP_OK;
-}
-
-sp_status segpaged_build(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int32_t page_size,
-                         const int32_t* ctx_len, const int32_t* q_len, const sp_head_policy* pol,
-                         const void* k_dense, const void* v_dense, const int32_t* free_pages,
-                         int64_t n_free, int64_t n_phys, void* k_pool, void* v_pool,
-                         int32_t* seg_table, int32_t* kv_len, int32_t* v2p, hipStream_t stream) {
-  return segpaged_build_layers(dtype, 1, B, Hkv, D, page_size, ctx_len, q_len, pol, k_dense,
-                               v_dense, free_pages, n_free, n_phys, k_pool, v_pool, seg_table,
-                               kv_len, v2p, stream);
-}
-
-sp_status segpaged_build_layers(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv,
-                                int32_t D, int32_t page_size, const int32_t* ctx_len,
-                                const int32_t* q_len, const sp_head_policy* pol,
-                                const void* k_dense, const void* v_dense,
-                                const int32_t* free_pages, int64_t n_free, int64_t n_phys,
-                                void* k_pool, void* v_pool, int32_t* seg_table, int32_t* kv_len,
-                                int32_t* v2p, hipStream_t stream) {
+// Build of n_layers layers (growable when `reserve` is not null: single layer only).
+sp_status build_impl(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv, int32_t D,
+                     int32_t page_size, const int32_t* ctx_len, const int32_t* q_len,
+                     const int32_t* reserve, const sp_head_policy* pol, const void* k_dense,
+                     const void* v_dense, const int32_t* free_pages, int64_t n_free,
+                     int64_t n_phys, void* k_pool, void* v_pool, int32_t* seg_table,
+                     int32_t* kv_len, int32_t* v2p, hipStream_t stream) {
   sp_status st = check_dtype_dim(dtype, D);
   if (st != SP_OK) return st;
-  st = check_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size);
-  if (st != SP_OK) return st;
   if (n_free < 0 || n_phys < 0) return SP_ERR_INVALID_ARG;
+  Layout lay;
+  st = layout_impl(n_layers, B, ctx_len, q_len, reserve, Hkv, pol, page_size, &lay);
+  if (st != SP_OK) return st;
   int64_t t_total = 0;
   for (int32_t b = 0; b < B; ++b) t_total += ctx_len[b];
   if (int64_t(n_layers) * t_total > 0x7fffffffLL) return SP_ERR_UNSUPPORTED;  // int32 rows
-  Layout lay;
-  st = make_layout_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size, &lay);
-  if (st != SP_OK) return st;
   if (B == 0) return SP_OK;
   if (seg_table == nullptr || kv_len == nullptr) return SP_ERR_INVALID_ARG;
   const int64_t n_virt = lay.n_virt;
@@ -326,6 +270,151 @@ sp_status segpaged_build_layers(sp_dtype dtype, int32_t n_layers, int32_t B, int
     }
   }
   return flush();
+}
+
+// Shape of a table-driven decode call: one query per request; ctx_hint only balances the
+// plan's KV splits (null: every request gets the same weight).
+sp_status table_decode_shape(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                             int32_t P, const int32_t* ctx_hint, const sp_head_policy* pol,
+                             std::vector<int32_t>* hint, std::vector<int32_t>* ones, Shape* s) {
+  if (B < 0) return SP_ERR_INVALID_ARG;
+  hint->assign(size_t(B), 1);
+  ones->assign(size_t(B), 1);
+  for (int32_t b = 0; b < B; ++b) {
+    if (ctx_hint != nullptr) {
+      if (ctx_hint[b] < 1) return SP_ERR_INVALID_ARG;
+      (*hint)[size_t(b)] = ctx_hint[b];
+    }
+  }
+  *s = make_shape(kModePaged, dtype, B, Hq, Hkv, D, P, hint->data(), ones->data(), pol);
+  sp_status st = check_shape(*s);
+  if (st != SP_OK) return st;
+  for (int32_t h = 0; h < Hkv; ++h)
+    if (pol[h].kind == SP_LOCAL_ADAPTIVE) return SP_ERR_UNSUPPORTED;
+  return SP_OK;
+}
+
+sp_status table_decode_plan(const Shape& s, Plan* plan) {
+  int32_t gp = 0, gd = 0;
+  sp_status st = grids(s, &gp, &gd);
+  if (st != SP_OK) return st;
+  return make_plan(s, gp, gd, plan, /*table_decode=*/true);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* segpaged_status_string(int status) {
+  switch (status) {
+    case SP_OK: return "SP_OK";
+    case SP_ERR_INVALID_ARG: return "SP_ERR_INVALID_ARG: invalid argument";
+    case SP_ERR_UNSUPPORTED: return "SP_ERR_UNSUPPORTED: unsupported shape, dtype or size";
+    case SP_ERR_POOL_TOO_SMALL: return "SP_ERR_POOL_TOO_SMALL: free list shorter than needed";
+    case SP_ERR_WORKSPACE_TOO_SMALL: return "SP_ERR_WORKSPACE_TOO_SMALL: workspace too small";
+    case SP_ERR_HIP: return "SP_ERR_HIP: HIP runtime error";
+    case SP_ERR_PLAN_MISMATCH: return "SP_ERR_PLAN_MISMATCH: workspace planned for other arguments";
+    case SP_ERR_SEGMENT_FULL: return "SP_ERR_SEGMENT_FULL: no owned page left for an appended token";
+    default: return "unknown status";
+  }
+}
+
+sp_status segpaged_plan_pages(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                              int32_t Hkv, const sp_head_policy* pol, int32_t page_size,
+                              int64_t* n_pages_needed) {
+  return segpaged_plan_pages_layers(1, B, ctx_len, q_len, Hkv, pol, page_size, n_pages_needed);
+}
+
+sp_status segpaged_plan_pages_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len,
+                                     const int32_t* q_len, int32_t Hkv,
+                                     const sp_head_policy* pol, int32_t page_size,
+                                     int64_t* n_pages_needed) {
+  if (n_pages_needed == nullptr) return SP_ERR_INVALID_ARG;
+  Layout lay;
+  sp_status st = layout_impl(n_layers, B, ctx_len, q_len, nullptr, Hkv, pol, page_size, &lay);
+  if (st != SP_OK) return st;
+  *n_pages_needed = lay.n_virt;
+  return SP_OK;
+}
+
+sp_status segpaged_layout_tables(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                                 int32_t Hkv, const sp_head_policy* pol, int32_t page_size,
+                                 int32_t* seg_table, int32_t* kv_len) {
+  return segpaged_layout_tables_layers(1, B, ctx_len, q_len, Hkv, pol, page_size, seg_table,
+                                       kv_len);
+}
+
+sp_status segpaged_layout_tables_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len,
+                                        const int32_t* q_len, int32_t Hkv,
+                                        const sp_head_policy* pol, int32_t page_size,
+                                        int32_t* seg_table, int32_t* kv_len) {
+  if (seg_table == nullptr || kv_len == nullptr) return SP_ERR_INVALID_ARG;
+  Layout lay;
+  sp_status st = layout_impl(n_layers, B, ctx_len, q_len, nullptr, Hkv, pol, page_size, &lay);
+  if (st != SP_OK) return st;
+  layout_tables(lay, n_layers * B * Hkv, seg_table, kv_len);
+  return SP_OK;
+}
+
+sp_status segpaged_plan_pages_growable(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                                       const int32_t* reserve, int32_t Hkv,
+                                       const sp_head_policy* pol, int32_t page_size,
+                                       int64_t* n_pages_needed) {
+  if (n_pages_needed == nullptr || reserve == nullptr) return SP_ERR_INVALID_ARG;
+  Layout lay;
+  sp_status st = layout_impl(1, B, ctx_len, q_len, reserve, Hkv, pol, page_size, &lay);
+  if (st != SP_OK) return st;
+  *n_pages_needed = lay.n_virt;
+  return SP_OK;
+}
+
+sp_status segpaged_layout_tables_growable(int32_t B, const int32_t* ctx_len,
+                                          const int32_t* q_len, const int32_t* reserve,
+                                          int32_t Hkv, const sp_head_policy* pol,
+                                          int32_t page_size, int32_t* seg_table,
+                                          int32_t* kv_len) {
+  if (seg_table == nullptr || kv_len == nullptr || reserve == nullptr) return SP_ERR_INVALID_ARG;
+  Layout lay;
+  sp_status st = layout_impl(1, B, ctx_len, q_len, reserve, Hkv, pol, page_size, &lay);
+  if (st != SP_OK) return st;
+  layout_tables(lay, B * Hkv, seg_table, kv_len);
+  return SP_OK;
+}
+
+sp_status segpaged_build_growable(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D,
+                                  int32_t page_size, const int32_t* ctx_len,
+                                  const int32_t* q_len, const int32_t* reserve,
+                                  const sp_head_policy* pol, const void* k_dense,
+                                  const void* v_dense, const int32_t* free_pages, int64_t n_free,
+                                  int64_t n_phys, void* k_pool, void* v_pool,
+                                  int32_t* seg_table, int32_t* kv_len, int32_t* v2p,
+                                  hipStream_t stream) {
+  if (reserve == nullptr) return SP_ERR_INVALID_ARG;
+  return build_impl(dtype, 1, B, Hkv, D, page_size, ctx_len, q_len, reserve, pol, k_dense,
+                    v_dense, free_pages, n_free, n_phys, k_pool, v_pool, seg_table, kv_len, v2p,
+                    stream);
+}
+
+sp_status segpaged_build(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int32_t page_size,
+                         const int32_t* ctx_len, const int32_t* q_len, const sp_head_policy* pol,
+                         const void* k_dense, const void* v_dense, const int32_t* free_pages,
+                         int64_t n_free, int64_t n_phys, void* k_pool, void* v_pool,
+                         int32_t* seg_table, int32_t* kv_len, int32_t* v2p, hipStream_t stream) {
+  return segpaged_build_layers(dtype, 1, B, Hkv, D, page_size, ctx_len, q_len, pol, k_dense,
+                               v_dense, free_pages, n_free, n_phys, k_pool, v_pool, seg_table,
+                               kv_len, v2p, stream);
+}
+
+sp_status segpaged_build_layers(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv,
+                                int32_t D, int32_t page_size, const int32_t* ctx_len,
+                                const int32_t* q_len, const sp_head_policy* pol,
+                                const void* k_dense, const void* v_dense,
+                                const int32_t* free_pages, int64_t n_free, int64_t n_phys,
+                                void* k_pool, void* v_pool, int32_t* seg_table, int32_t* kv_len,
+                                int32_t* v2p, hipStream_t stream) {
+  return build_impl(dtype, n_layers, B, Hkv, D, page_size, ctx_len, q_len, nullptr, pol, k_dense,
+                    v_dense, free_pages, n_free, n_phys, k_pool, v_pool, seg_table, kv_len, v2p,
+                    stream);
 }
 
 sp_status segpaged_attention_workspace_size(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
@@ -436,6 +525,139 @@ sp_status segpaged_dense_mask_attention(sp_dtype dtype, int32_t B, int32_t Hq, i
   return run_attention(make_shape(kModeDense, dtype, B, Hq, Hkv, D, 64, ctx_len, q_len, pol), q,
                        k_dense, v_dense, 0, nullptr, nullptr, nullptr, softmax_scale, o,
                        workspace, ws_bytes, stream, nullptr, nullptr);
+}
+
+sp_status segpaged_decode_workspace_size(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                         int32_t D, int32_t page_size, const int32_t* ctx_hint,
+                                         const sp_head_policy* pol, size_t* bytes) {
+  if (bytes == nullptr) return SP_ERR_INVALID_ARG;
+  std::vector<int32_t> hint, ones;
+  Shape s;
+  sp_status st = table_decode_shape(dtype, B, Hq, Hkv, D, page_size, ctx_hint, pol, &hint,
+                                    &ones, &s);
+  if (st != SP_OK) return st;
+  Plan plan;
+  st = table_decode_plan(s, &plan);
+  if (st != SP_OK) return st;
+  *bytes = plan.bytes;
+  return SP_OK;
+}
+
+sp_status segpaged_decode_plan(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                               int32_t page_size, const int32_t* ctx_hint,
+                               const sp_head_policy* pol, void* workspace, size_t ws_bytes,
+                               hipStream_t stream) {
+  std::vector<int32_t> hint, ones;
+  Shape s;
+  sp_status st = table_decode_shape(dtype, B, Hq, Hkv, D, page_size, ctx_hint, pol, &hint,
+                                    &ones, &s);
+  if (st != SP_OK) return st;
+  if (workspace == nullptr) return SP_ERR_INVALID_ARG;
+  Plan plan;
+  st = table_decode_plan(s, &plan);
+  if (st != SP_OK) return st;
+  if (ws_bytes < plan.bytes) return SP_ERR_WORKSPACE_TOO_SMALL;
+  std::vector<uint8_t> buf;
+  serialize_plan(plan, &buf);
+  if (hipMemcpyAsync(workspace, buf.data(), buf.size(), hipMemcpyHostToDevice, stream) !=
+      hipSuccess)
+    return SP_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SP_ERR_HIP;
+  return SP_OK;
+}
+
+sp_status segpaged_decode(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                          int32_t page_size, const sp_head_policy* pol, const void* q,
+                          const void* k_pool, const void* v_pool, int64_t n_phys,
+                          const int32_t* seg_table, const int32_t* kv_len, const int32_t* v2p,
+                          float softmax_scale, void* o, void* workspace, size_t ws_bytes,
+                          hipStream_t stream) {
+  std::vector<int32_t> hint, ones;
+  Shape s;
+  sp_status st = table_decode_shape(dtype, B, Hq, Hkv, D, page_size, nullptr, pol, &hint,
+                                    &ones, &s);
+  if (st != SP_OK) return st;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return SP_ERR_INVALID_ARG;
+  if (B == 0) return SP_OK;
+  if (q == nullptr || k_pool == nullptr || v_pool == nullptr || o == nullptr ||
+      workspace == nullptr || seg_table == nullptr || kv_len == nullptr || v2p == nullptr ||
+      n_phys < 1)
+    return SP_ERR_INVALID_ARG;
+  if (ws_bytes < size_t(kHeaderBytes)) return SP_ERR_WORKSPACE_TOO_SMALL;
+  int32_t gp = 0, gd = 0;
+  st = grids(s, &gp, &gd);
+  if (st != SP_OK) return st;
+  AttnParams p;
+  p.q = q;
+  p.o = o;
+  p.k = k_pool;
+  p.v = v_pool;
+  p.seg_table = seg_table;
+  p.kv_len = kv_len;
+  p.v2p = v2p;
+  p.n_phys = n_phys;
+  p.ws = static_cast<uint8_t*>(workspace);
+  p.signature = table_decode_signature(s, gd);
+  p.ws_bytes = ws_bytes;
+  p.Hq = s.Hq;
+  p.Hkv = s.Hkv;
+  p.G = s.Hq / s.Hkv;
+  p.P = s.P;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  if (launch_attention(s.dtype, s.D, kModePaged, true, gd, p, stream) != hipSuccess)
+    return SP_ERR_HIP;
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != SP_OK) return st;
+  if (launch_combine(s.dtype, s.D, 4 * cus, p, stream) != hipSuccess) return SP_ERR_HIP;
+  return SP_OK;
+}
+
+sp_status segpaged_append(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int32_t page_size,
+                          const sp_head_policy* pol, const int32_t* n_new, const void* k_new,
+                          const void* v_new, void* k_pool, void* v_pool, int64_t n_phys,
+                          int32_t* seg_table, int32_t* kv_len, int32_t* v2p, int64_t n_virt,
+                          int32_t* error, hipStream_t stream) {
+  sp_status st = check_dtype_dim(dtype, D);
+  if (st != SP_OK) return st;
+  st = check_page_size(page_size);
+  if (st != SP_OK) return st;
+  if (B < 0 || Hkv < 1 || pol == nullptr) return SP_ERR_INVALID_ARG;
+  if (Hkv > kMaxAppendHeads) return SP_ERR_UNSUPPORTED;
+  for (int32_t h = 0; h < Hkv; ++h) {
+    if (pol[h].kind == SP_LOCAL_ADAPTIVE) return SP_ERR_UNSUPPORTED;
+    if (pol[h].kind != SP_GLOBAL && pol[h].kind != SP_LOCAL) return SP_ERR_INVALID_ARG;
+    if (pol[h].kind == SP_LOCAL && (pol[h].sink < 0 || pol[h].window < 1))
+      return SP_ERR_INVALID_ARG;
+  }
+  if (int64_t(B) * Hkv > 0x7fffffffLL) return SP_ERR_UNSUPPORTED;
+  if (B == 0) return SP_OK;
+  if (k_new == nullptr || v_new == nullptr || k_pool == nullptr || v_pool == nullptr ||
+      seg_table == nullptr || kv_len == nullptr || v2p == nullptr || error == nullptr ||
+      n_phys < 1 || n_virt < 1 || n_virt > 0x7fffffffLL)
+    return SP_ERR_INVALID_ARG;
+  AppendParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.n_new = n_new;
+  p.kp = k_pool;
+  p.vp = v_pool;
+  p.seg_table = seg_table;
+  p.kv_len = kv_len;
+  p.v2p = v2p;
+  p.error = error;
+  p.n_phys = n_phys;
+  p.n_virt = n_virt;
+  p.Hkv = Hkv;
+  p.P = page_size;
+  for (int32_t h = 0; h < Hkv; ++h) {
+    p.pol[h][0] = pol[h].kind;
+    p.pol[h][1] = pol[h].kind == SP_LOCAL ? pol[h].sink : 0;
+    p.pol[h][2] = pol[h].kind == SP_LOCAL ? pol[h].window : 1;
+  }
+  if (launch_append(dtype, D, B * Hkv, p, stream) != hipSuccess) return SP_ERR_HIP;
+  return SP_OK;
 }
 
 }  // extern "C"

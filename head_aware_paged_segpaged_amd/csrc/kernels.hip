@@ -847,6 +847,27 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
 constexpr int kSub = 16;      // keys per decode sub-step
 constexpr int kDecAhead = 3;  // sub-steps of K and V in flight ahead of the one computed
 
+// A decode item of a table-driven plan (ra_seg < 0) carries only its split: split c_begin of
+// c_end over all tokens its (request, KV head) stores, as the device tables hold them when the
+// kernel runs (segment 0, then segment 1). The query is the newest stored token: in decode the
+// request's last context position, which every head stores.
+__device__ __forceinline__ void table_item(WorkItem& w, ItemKV& kv) {
+  const int na = kv.ntok0, nb = kv.ntok1;
+  const int sa = (na + kChunk - 1) / kChunk, sb = (nb + kChunk - 1) / kChunk;
+  const int64_t n = sa + sb;
+  const int k = w.c_begin, ns = max(w.c_end, 1);
+  w.ra_seg = 0;
+  w.ra_begin = 0;
+  w.ra_end = na;
+  w.rb_seg = 1;
+  w.rb_begin = 0;
+  w.rb_end = nb;
+  w.c_begin = int(n * k / ns);
+  w.c_end = int(n * (k + 1) / ns);
+  w.p0 = (nb > 0 ? kv.pos1 + nb : kv.pos0 + na) - 1;
+  kv.n_ra = sa;
+}
+
 // One decode sub-step: rows [vlo, vhi) of 16 are valid; `off` is the element offset of row 0
 // in the pool or the dense K/V (0 when there is no valid row).
 struct Sub {
@@ -991,11 +1012,14 @@ __global__ void __launch_bounds__(64) decode_kernel(AttnParams p) {
     if (lane == 0) it = pop_item(p.ws, hd->decode_q, kOffDecodeCnt, xcd, exhausted, first);
     it = uniform(it);
     if (it < 0) break;
-    const WorkItem w = load_item(items, it);
+    WorkItem w = load_item(items, it);
     SubSrc src;
     {
       ItemKV kv;
       load_item_kv(p, w, kDense, kv, p.ws);
+      if constexpr (!kDense) {
+        if (w.ra_seg < 0) table_item(w, kv);
+      }
       src = sub_source(w, kv, kDense, p.P);
     }
     const int32_t* ph = pol + (w.b * p.Hkv + w.h) * 3;  // effective policy of (request, head)
@@ -1305,6 +1329,159 @@ __global__ void __launch_bounds__(256) build_kernel(BuildParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Decode append: one wave per (request, KV head) writes the request's new token into the
+// head's pages and updates its table row (growable layout, see include/segpaged.h). LOCAL
+// heads keep their recent segment as a ring of whole pages: pages whose tokens all fell out of
+// the window are dropped from its front and their physical pages rotate to its back, so the
+// head's page use stays constant.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ void append_error(int32_t* err, int code) {
+  if (threadIdx.x == 0) atomicCAS(reinterpret_cast<int*>(err), 0, code);
+}
+
+// Rotates x[0 .. n) left by k (0 < k < n) with the 64 lanes of one wave. Up to 256 entries:
+// every lane loads its four sources, the wave waits, then stores. Longer rings: three
+// reversals (of [0, k), [k, n), then [0, n)); within a reversal every pair of entries belongs
+// to one lane and one iteration.
+__device__ void rotate_left(int32_t* x, int n, int k) {
+  const int lane = threadIdx.x;
+  if (n <= 256) {
+    int v[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = lane + 64 * c;
+      int src = j + k;
+      if (src >= n) src -= n;
+      v[c] = j < n ? x[src] : 0;
+    }
+    __syncthreads();  // every load has returned before any entry is overwritten
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = lane + 64 * c;
+      if (j < n) x[j] = v[c];
+    }
+    return;
+  }
+  auto reverse = [&](int a, int m) {
+    for (int i = lane; i < m / 2; i += 64) {
+      const int l = x[a + i], r = x[a + m - 1 - i];
+      x[a + i] = r;
+      x[a + m - 1 - i] = l;
+    }
+  };
+  reverse(0, k);
+  reverse(k, n - k);
+  __syncthreads();
+  reverse(0, n);
+}
+
+template <class E, int D>
+__global__ void __launch_bounds__(64) append_kernel(AppendParams p) {
+  using S = typename E::S;
+  const int b = blockIdx.x / p.Hkv, h = blockIdx.x - b * p.Hkv;
+  if (p.n_new != nullptr) {
+    const int nn = uniform(p.n_new[b]);
+    if (nn == 0) return;
+    if (nn != 1) {
+      append_error(p.error, SP_ERR_INVALID_ARG);
+      return;
+    }
+  }
+  int32_t* e = p.seg_table + (int64_t(b) * p.Hkv + h) * 8;
+  int pos[2], ntok[2], vs[2], own[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    pos[s] = uniform(e[4 * s + 0]);
+    ntok[s] = uniform(e[4 * s + 1]);
+    vs[s] = uniform(e[4 * s + 2]);
+    own[s] = uniform(e[4 * s + 3]);
+  }
+  const int kind = p.pol[h][0], sink = p.pol[h][1], window = p.pol[h][2];
+  const int P = p.P;
+  // Old context length: one past the newest stored token.
+  int L = -1;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    if (ntok[s] > 0) L = max(L, pos[s] + ntok[s]);
+  if (L < 0 || ntok[0] < 0 || ntok[1] < 0) {
+    append_error(p.error, SP_ERR_INVALID_ARG);
+    return;
+  }
+  const int r0 = max(0, L + 1 - window);  // first window position of the query at L
+  int ring = -1;
+  if (kind == SP_LOCAL) {
+    if (sink == 0) {
+      ring = 0;
+    } else if (own[1] > 0) {
+      ring = 1;
+    } else {
+      // One segment (0, L) holding sink and window: split once the window start reaches the
+      // first page boundary past the sink.
+      const int s_pages = (sink + P - 1) / P, s_pg = s_pages * P;
+      if (r0 >= s_pg) {
+        pos[1] = s_pg;
+        ntok[1] = ntok[0] - s_pg;
+        vs[1] = vs[0] + s_pages;
+        own[1] = own[0] - s_pages;
+        ntok[0] = sink;
+        own[0] = s_pages;
+        ring = 1;
+      }
+    }
+  }
+  int k = 0;  // ring pages dropped by this append
+  if (ring >= 0) {
+    const int lag = r0 - pos[ring];
+    k = lag > 0 ? lag / P : 0;
+    pos[ring] += k * P;
+    ntok[ring] -= k * P;
+  }
+  const int t = ring >= 0 ? ring : 0;
+  const int slot_idx = ntok[t];
+  const int page = slot_idx / P;
+  if (own[t] < 1 || page >= own[t] || k > own[t] || vs[t] < 0 ||
+      int64_t(vs[t]) + own[t] > p.n_virt) {
+    append_error(p.error, own[t] >= 1 && page >= own[t] ? SP_ERR_SEGMENT_FULL
+                                                         : SP_ERR_INVALID_ARG);
+    return;
+  }
+  // Physical page of the new token, read before the rotation: after rotating left by k,
+  // position j of the segment's page list holds what was at (j + k) mod own.
+  int src = page + k;
+  if (src >= own[t]) src -= own[t];
+  const int phys = uniform(p.v2p[vs[t] + src]);
+  if (uint32_t(phys) >= uint64_t(p.n_phys)) {
+    append_error(p.error, SP_ERR_INVALID_ARG);
+    return;
+  }
+  if (k > 0 && k < own[t]) rotate_left(p.v2p + vs[t], own[t], k);
+
+  // The token's K and V rows: D elements each, as 4-byte words.
+  constexpr int kWords = D * int(sizeof(S)) / 4;
+  const int64_t row = (int64_t(b) * p.Hkv + h) * D;
+  const int64_t dst = (int64_t(phys) * P + (slot_idx - page * P)) * D;
+  const uint32_t* ks = reinterpret_cast<const uint32_t*>(static_cast<const S*>(p.k_new) + row);
+  const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(static_cast<const S*>(p.v_new) + row);
+  uint32_t* kd = reinterpret_cast<uint32_t*>(static_cast<S*>(p.kp) + dst);
+  uint32_t* vd = reinterpret_cast<uint32_t*>(static_cast<S*>(p.vp) + dst);
+  for (int i = threadIdx.x; i < kWords; i += 64) {
+    kd[i] = ks[i];
+    vd[i] = vsrc[i];
+  }
+  ntok[t] += 1;
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      e[4 * s + 0] = pos[s];
+      e[4 * s + 1] = ntok[s];
+      e[4 * s + 2] = vs[s];
+      e[4 * s + 3] = own[s];
+    }
+    p.kv_len[int64_t(b) * p.Hkv + h] = ntok[0] + ntok[1];
+  }
+}
+
 template <class E, int D, int MODE>
 int occ_of(bool decode) {
   int n = 0;
@@ -1374,6 +1551,19 @@ hipError_t launch_combine(int32_t dtype, int32_t D, int grid, const AttnParams& 
   } else {
     if (D == 64) combine_kernel<F32, 64><<<grid, 256, 0, stream>>>(p);
     else combine_kernel<F32, 128><<<grid, 256, 0, stream>>>(p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_append(int32_t dtype, int32_t D, int grid, const AppendParams& p,
+                         hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  if (dtype == SP_BF16) {
+    if (D == 64) append_kernel<BF16, 64><<<grid, 64, 0, stream>>>(p);
+    else append_kernel<BF16, 128><<<grid, 64, 0, stream>>>(p);
+  } else {
+    if (D == 64) append_kernel<F32, 64><<<grid, 64, 0, stream>>>(p);
+    else append_kernel<F32, 128><<<grid, 64, 0, stream>>>(p);
   }
   return hipGetLastError();
 }

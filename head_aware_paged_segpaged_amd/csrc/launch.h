@@ -44,6 +44,23 @@ struct BuildParams {
   BuildSeg seg[kMaxBuildSegs];
 };
 
+constexpr int kMaxAppendHeads = 128;
+
+struct AppendParams {
+  const void* k_new;    // [B][Hkv][D]: the new token of every request
+  const void* v_new;
+  const int32_t* n_new;  // [B] 0 or 1, or null (every request appends)
+  void* kp;
+  void* vp;
+  int32_t* seg_table;
+  int32_t* kv_len;
+  int32_t* v2p;
+  int32_t* error;  // device word: first error code of the launch
+  int64_t n_phys, n_virt;
+  int32_t Hkv, P;
+  int32_t pol[kMaxAppendHeads][3];  // (kind, sink, window) per KV head
+};
+
 // Resident work groups per compute unit of the persistent attention kernels.
 int attention_occupancy(int32_t dtype, int32_t D, int32_t mode, bool decode);
 hipError_t launch_attention(int32_t dtype, int32_t D, int32_t mode, bool decode, int grid,
@@ -51,5 +68,7 @@ hipError_t launch_attention(int32_t dtype, int32_t D, int32_t mode, bool decode,
 hipError_t launch_combine(int32_t dtype, int32_t D, int grid, const AttnParams& p,
                           hipStream_t stream);
 hipError_t launch_build(int32_t dtype, int32_t D, const BuildParams& p, hipStream_t stream);
+hipError_t launch_append(int32_t dtype, int32_t D, int grid, const AppendParams& p,
+                         hipStream_t stream);
 
 }  // namespace sp

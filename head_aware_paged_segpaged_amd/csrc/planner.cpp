@@ -118,14 +118,49 @@ int head_segments(const sp_head_policy& pol_in, int32_t L, int32_t q, int32_t ou
   return 2;
 }
 
+sp_status check_growable(int32_t B, const int32_t* ctx_len, const int32_t* reserve, int32_t Hkv,
+                         const sp_head_policy* pol) {
+  if (B > 0 && reserve == nullptr) return SP_ERR_INVALID_ARG;
+  for (int32_t h = 0; h < Hkv; ++h)
+    if (pol[h].kind == SP_LOCAL_ADAPTIVE) return SP_ERR_UNSUPPORTED;
+  for (int32_t b = 0; b < B; ++b) {
+    if (reserve[b] < 0 || (reserve[b] > 0 && ctx_len[b] < 1)) return SP_ERR_INVALID_ARG;
+    if (int64_t(ctx_len[b]) + reserve[b] > kInt32Max) return SP_ERR_UNSUPPORTED;
+  }
+  return SP_OK;
+}
+
+void owned_pages(const sp_head_policy& pol, int nseg, const int32_t pos[2],
+                 const int32_t ntok[2], int64_t L, int64_t lmax, int32_t P, int64_t own[2]) {
+  for (int s = 0; s < nseg; ++s) own[s] = ceil_div(ntok[s], P);
+  if (nseg == 0 || lmax <= L) return;
+  if (pol.kind == SP_GLOBAL) {
+    own[0] = ceil_div(lmax, P);
+    return;
+  }
+  const int64_t W = pol.window, S = pol.sink;
+  const int64_t ring_max = W + P - 1;  // most tokens a ring holds once it recycles pages
+  if (S > 0 && nseg == 1) {
+    // Sink and window in one segment (0, L): grows whole until the window start reaches the
+    // first page boundary past the sink, then becomes sink pages + a ring from that boundary.
+    const int64_t s_pages = ceil_div(S, P), s_pg = s_pages * P;
+    int64_t o = std::max(own[0], ceil_div(std::min(lmax, s_pg + W - 1), P));
+    if (lmax >= s_pg + W) o = std::max(o, s_pages + ceil_div(std::min(lmax - s_pg, ring_max), P));
+    own[0] = o;
+    return;
+  }
+  const int r = nseg - 1;  // the ring: the only segment (sink 0) or the one after the sink
+  own[r] = std::max(own[r], ceil_div(std::min(lmax - pos[r], ring_max), P));
+}
+
 sp_status make_layout(int32_t B, const int32_t* ctx_len, const int32_t* q_len, int32_t Hkv,
                       const sp_head_policy* pol, int32_t P, Layout* out) {
-  return make_layout_layers(1, B, ctx_len, q_len, Hkv, pol, P, out);
+  return make_layout_layers(1, B, ctx_len, q_len, Hkv, pol, P, nullptr, out);
 }
 
 sp_status make_layout_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len,
                              const int32_t* q_len, int32_t Hkv, const sp_head_policy* pol,
-                             int32_t P, Layout* out) {
+                             int32_t P, const int32_t* reserve, Layout* out) {
   out->heads.assign(size_t(n_layers) * B * Hkv, HeadLayout{});
   int64_t v = 0;
   for (int32_t b = 0; b < B; ++b) {
@@ -133,15 +168,20 @@ sp_status make_layout_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len
       for (int32_t h = 0; h < Hkv; ++h) {
         HeadLayout& hl = out->heads[(size_t(l) * B + b) * Hkv + h];
         int32_t pos[2] = {0, 0}, ntok[2] = {0, 0};
-        hl.nseg = head_segments(pol[size_t(l) * Hkv + h], ctx_len[b], q_len[b], pos, ntok);
+        const sp_head_policy& hp = pol[size_t(l) * Hkv + h];
+        hl.nseg = head_segments(hp, ctx_len[b], q_len[b], pos, ntok);
         hl.kv_len = 0;
+        int64_t own[2] = {0, 0};
+        owned_pages(hp, hl.nseg, pos, ntok, ctx_len[b],
+                    int64_t(ctx_len[b]) + (reserve ? reserve[b] : 0), P, own);
         for (int s = 0; s < 2; ++s) {
           Segment& sg = hl.seg[s];
           if (s < hl.nseg) {
+            if (v + own[s] > kInt32Max) return SP_ERR_UNSUPPORTED;
             sg.pos = pos[s];
             sg.ntok = ntok[s];
             sg.vstart = int32_t(v);
-            sg.npages = int32_t(ceil_div(ntok[s], P));
+            sg.npages = int32_t(own[s]);
             v += sg.npages;
             hl.kv_len += ntok[s];
           } else {
@@ -178,6 +218,18 @@ uint64_t shape_signature(const Shape& s, int32_t slots_prefill, int32_t slots_de
   for (int64_t f : fields) h = fnv(h, uint64_t(f));
   for (int32_t b = 0; b < s.B; ++b) h = fnv(h, (uint64_t(uint32_t(s.ctx_len[b])) << 32) |
                                                    uint32_t(s.q_len[b]));
+  for (int32_t i = 0; i < s.Hkv; ++i) {
+    h = fnv(h, uint64_t(uint32_t(s.pol[i].kind)));
+    if (s.pol[i].kind != SP_GLOBAL)
+      h = fnv(h, (uint64_t(uint32_t(s.pol[i].sink)) << 32) | uint32_t(s.pol[i].window));
+  }
+  return h;
+}
+
+uint64_t table_decode_signature(const Shape& s, int32_t slots_decode) {
+  uint64_t h = 0xcbf29ce484222325ull;
+  const int64_t fields[] = {kModeTableDecode, s.dtype, s.B, s.Hq, s.Hkv, s.D, s.P, slots_decode};
+  for (int64_t f : fields) h = fnv(h, uint64_t(f));
   for (int32_t i = 0; i < s.Hkv; ++i) {
     h = fnv(h, uint64_t(uint32_t(s.pol[i].kind)));
     if (s.pol[i].kind != SP_GLOBAL)
@@ -235,7 +287,8 @@ void tile_ranges(const Shape& s, const HeadLayout* hl, const sp_head_policy& pol
 struct Tile {
   WorkItem w;
   int32_t steps;
-  int32_t split;  // index of this split within its tile
+  int32_t split;   // index of this split within its tile
+  int32_t nsplit;  // splits of its tile
 };
 
 // Splits long tiles along KV so that no item is much longer than the average load of one
@@ -255,6 +308,7 @@ void split_tiles(std::vector<Tile>& tiles, int32_t slots, int32_t min_split, int
     if (ns == 1) {
       Tile x = t;
       x.w.part = -1;
+      x.nsplit = 1;
       items->push_back(x);
       continue;
     }
@@ -269,6 +323,7 @@ void split_tiles(std::vector<Tile>& tiles, int32_t slots, int32_t min_split, int
       x.w.part = part0 + k;
       x.steps = c1 - c0;
       x.split = k;
+      x.nsplit = ns;
       items->push_back(x);
     }
     combine->push_back(CombineItem{t.w.b, t.w.h, t.w.tq0, t.w.nq, part0, ns, t.w.q_row0, kind});
@@ -306,7 +361,8 @@ void make_queues(std::vector<Tile>& items, std::vector<WorkItem>* out, int32_t* 
 
 }  // namespace
 
-sp_status make_plan(const Shape& s, int32_t slots_prefill, int32_t slots_decode, Plan* out) {
+sp_status make_plan(const Shape& s, int32_t slots_prefill, int32_t slots_decode, Plan* out,
+                    bool table_decode) {
   Layout lay;
   if (s.mode == kModePaged) {
     sp_status st = make_layout(s.B, s.ctx_len, s.q_len, s.Hkv, s.pol, s.P, &lay);
@@ -362,6 +418,20 @@ sp_status make_plan(const Shape& s, int32_t slots_prefill, int32_t slots_decode,
   int32_t n_part_pre = 0, n_part_dec = 0;
   split_tiles(pre_tiles, slots_prefill, /*min_split=*/8, 0, &pre_items, &combine, &n_part_pre);
   split_tiles(dec_tiles, slots_decode, /*min_split=*/32, 1, &dec_items, &combine, &n_part_dec);
+  if (table_decode) {
+    // Each decode item keeps only its split fraction (split c_begin of c_end); the kernel takes
+    // the head's stored tokens and query position from the device tables when it runs.
+    for (Tile& t : dec_items) {
+      WorkItem& w = t.w;
+      w.ra_seg = -1;
+      w.ra_begin = w.ra_end = 0;
+      w.rb_seg = 0;
+      w.rb_begin = w.rb_end = 0;
+      w.c_begin = t.split;
+      w.c_end = t.nsplit;
+      w.p0 = 0;
+    }
+  }
 
   WsHeader& hd = out->hdr;
   std::memset(&hd, 0, sizeof(hd));
@@ -381,7 +451,8 @@ sp_status make_plan(const Shape& s, int32_t slots_prefill, int32_t slots_decode,
   }
 
   hd.magic = kMagic;
-  hd.signature = shape_signature(s, slots_prefill, slots_decode);
+  hd.signature = table_decode ? table_decode_signature(s, slots_decode)
+                              : shape_signature(s, slots_prefill, slots_decode);
   hd.n_prefill = int32_t(out->prefill.size());
   hd.n_decode = int32_t(out->decode.size());
   hd.n_combine = int32_t(out->combine.size());

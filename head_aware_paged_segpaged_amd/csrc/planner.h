@@ -55,10 +55,20 @@ int head_segments(const sp_head_policy& pol, int32_t L, int32_t q, int32_t out_p
 
 sp_status make_layout(int32_t B, const int32_t* ctx_len, const int32_t* q_len, int32_t Hkv,
                       const sp_head_policy* pol, int32_t P, Layout* out);
-// The same for n_layers layers sharing one page pool; pol is [n_layers][Hkv].
+// The same for n_layers layers sharing one page pool; pol is [n_layers][Hkv]. With `reserve`
+// (host [B], or null) the layout is growable: each segment owns the pages it needs while its
+// request's context grows by reserve[b] decode tokens (Segment::npages = pages owned).
 sp_status make_layout_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len,
                              const int32_t* q_len, int32_t Hkv, const sp_head_policy* pol,
-                             int32_t P, Layout* out);
+                             int32_t P, const int32_t* reserve, Layout* out);
+
+// Arguments of a growable layout: reserve[b] >= 0, a non-empty context where reserve[b] > 0,
+// no context-adaptive heads (their window moves with the context).
+sp_status check_growable(int32_t B, const int32_t* ctx_len, const int32_t* reserve, int32_t Hkv,
+                         const sp_head_policy* pol);
+// Pages owned by each of the nseg segments of one head whose context L may grow to lmax.
+void owned_pages(const sp_head_policy& pol, int nseg, const int32_t pos[2],
+                 const int32_t ntok[2], int64_t L, int64_t lmax, int32_t P, int64_t own[2]);
 
 // Fills seg_table [B][Hkv][2][4] and kv_len [B][Hkv] from a layout.
 // seg_table [n_layers][B][Hkv][2][4] and kv_len [n_layers][B][Hkv] of a layout.
@@ -66,6 +76,8 @@ void layout_tables(const Layout& lay, int32_t n_heads_total, int32_t* seg_table,
                    int32_t* kv_len);
 
 uint64_t shape_signature(const Shape& s, int32_t slots_prefill, int32_t slots_decode);
+// Signature of a table-driven decode plan: shapes and policies, no lengths.
+uint64_t table_decode_signature(const Shape& s, int32_t slots_decode);
 
 struct Plan {
   WsHeader hdr;
@@ -76,7 +88,11 @@ struct Plan {
   size_t upload_bytes = 0;      // header + item arrays + policy (what the plan call copies)
 };
 
-sp_status make_plan(const Shape& s, int32_t slots_prefill, int32_t slots_decode, Plan* out);
+// table_decode: every request has one query (q_len all 1); the decode items are written in
+// their table-driven form (ra_seg = -1, split c_begin of c_end) and the plan carries
+// table_decode_signature. Lengths only balance the splits.
+sp_status make_plan(const Shape& s, int32_t slots_prefill, int32_t slots_decode, Plan* out,
+                    bool table_decode = false);
 
 // Header, counters (zero), item arrays and policy table as one host buffer of
 // plan.upload_bytes bytes, laid out exactly as in the workspace.

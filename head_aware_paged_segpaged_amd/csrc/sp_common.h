@@ -24,7 +24,7 @@ constexpr int kItemOverhead = 2;
 constexpr uint64_t kMagic = 0x5350414745445631ull;  // "SPAGEDV1"
 constexpr int kHeaderBytes = 4096;
 
-enum Mode : int32_t { kModePaged = 0, kModeDense = 1 };
+enum Mode : int32_t { kModePaged = 0, kModeDense = 1, kModeTableDecode = 2 };
 
 // One contiguous range of stored tokens of one segment: indices [begin, end) counted from the
 // segment's first stored token (for the dense path: dense rows of the request).

@@ -160,6 +160,101 @@ class SegPagedLayers:
         return B.segpaged_attention_check(self.workspaces[layer], stream)
 
 
+class SegPagedDecoder:
+    """One layer's growable layout for decoding: built once (pages reserved for ``reserve``
+    more tokens per request), then every step appends each request's new token and runs the
+    table-driven decode, all on the device (page "RedKnot SegPagedAttention runtime design",
+    section 3: LOCAL storage does not grow with the context; section 5: no layout work per
+    call). ``ctx_now`` tracks the lengths on the host only to size the decode splits."""
+
+    def __init__(self, dtype, Hq: int, Hkv: int, D: int, page_size: int, ctx_len, q_len, reserve,
+                 policy, device: str = "cuda"):
+        self.dtype = _dt(dtype)
+        self.Hq, self.Hkv, self.D, self.P = int(Hq), int(Hkv), int(D), int(page_size)
+        self.ctx_len = np.asarray(ctx_len, dtype=np.int32)
+        self.q_len = np.asarray(q_len, dtype=np.int32)
+        self.reserve = np.asarray(reserve, dtype=np.int32)
+        self.policy = np.asarray(policy, dtype=np.int32).reshape(self.Hkv, 3)
+        self.device = device
+        self.n_virt = B.segpaged_plan_pages_growable(self.ctx_len, self.q_len, self.reserve,
+                                                     self.policy, self.P)
+        self.ctx_now = self.ctx_len.copy()
+        self.k_pool = self.v_pool = None
+        self.seg_table = self.kv_len = self.v2p = None
+        self.error = None
+        self.workspace = None
+        self.n_phys = 0
+
+    def build(self, k_dense: torch.Tensor, v_dense: torch.Tensor, free_pages,
+              n_phys: int | None = None, stream=None) -> None:
+        self.n_phys = int(n_phys if n_phys is not None else max(self.n_virt, 1))
+        t = _TORCH[self.dtype]
+        self.k_pool = torch.empty((max(self.n_phys, 1), self.P, self.D), dtype=t,
+                                  device=self.device)
+        self.v_pool = torch.empty_like(self.k_pool)
+        Bn = max(len(self.ctx_len), 1)
+        n_tab, n_kl = Bn * self.Hkv * 8, Bn * self.Hkv
+        tables = torch.zeros((n_tab + n_kl + max(self.n_virt, 1) + 1,), dtype=torch.int32,
+                             device=self.device)
+        self.seg_table = tables[:n_tab].view(Bn, self.Hkv, 2, 4)
+        self.kv_len = tables[n_tab:n_tab + n_kl].view(Bn, self.Hkv)
+        self.v2p = tables[n_tab + n_kl:n_tab + n_kl + max(self.n_virt, 1)]
+        self.error = tables[-1:]
+        B.segpaged_build_growable(self.dtype, self.D, self.P, self.ctx_len, self.q_len,
+                                  self.reserve, self.policy, k_dense, v_dense,
+                                  np.asarray(free_pages, dtype=np.int32), self.n_phys,
+                                  self.k_pool, self.v_pool, self.seg_table, self.kv_len,
+                                  self.v2p, stream)
+        self.ctx_now = self.ctx_len.copy()
+
+    def plan(self, stream=None) -> None:
+        """(Re)plan the table-driven decode, with splits sized for the current lengths."""
+        n = B.segpaged_decode_workspace_size(self.dtype, self.Hq, self.Hkv, self.D, self.P,
+                                             self.ctx_now, self.policy)
+        if self.workspace is None or self.workspace.numel() < n:
+            self.workspace = torch.zeros((n,), dtype=torch.uint8, device=self.device)
+        B.segpaged_decode_plan(self.dtype, self.Hq, self.Hkv, self.D, self.P, self.ctx_now,
+                               self.policy, self.workspace, stream)
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor, n_new=None, stream=None) -> None:
+        """k_new, v_new: [B, Hkv, D]; n_new: None (every request) or 0/1 per request (host
+        array, copied to the device, or a device int32 tensor)."""
+        dev_n = None
+        if n_new is not None:
+            if isinstance(n_new, torch.Tensor) and n_new.is_cuda:
+                dev_n = n_new
+                host_n = n_new.cpu().numpy()
+            else:
+                host_n = np.asarray(n_new, dtype=np.int32)
+                dev_n = torch.from_numpy(host_n.copy()).to(self.device)
+            self.ctx_now = self.ctx_now + host_n.astype(np.int32)
+        else:
+            self.ctx_now = self.ctx_now + 1
+        B.segpaged_append(self.dtype, self.D, self.P, self.policy, dev_n, k_new, v_new,
+                          self.k_pool, self.v_pool, self.n_phys, self.seg_table, self.kv_len,
+                          self.v2p, self.error, stream)
+
+    def decode(self, q: torch.Tensor, scale: float, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+        """q: [B, Hq, D], one query per request at its newest position."""
+        if self.workspace is None:
+            self.plan(stream)
+        if out is None:
+            out = torch.empty_like(q)
+        B.segpaged_decode(self.dtype, self.Hq, self.Hkv, self.D, self.P, self.policy, q,
+                          self.k_pool, self.v_pool, self.n_phys, self.seg_table, self.kv_len,
+                          self.v2p, scale, out, self.workspace, stream)
+        return out
+
+    def check(self, stream=None) -> tuple[int, int]:
+        """(append error word, decode workspace error word); reading clears both."""
+        torch.cuda.synchronize()
+        a = int(self.error.item())
+        self.error.zero_()
+        d = B.segpaged_attention_check(self.workspace, stream) if self.workspace is not None else 0
+        return a, d
+
+
 class DenseMaskLayer:
     def __init__(self, dtype, Hq: int, Hkv: int, D: int, ctx_len, q_len, policy,
                  device: str = "cuda"):

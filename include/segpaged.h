@@ -15,6 +15,13 @@
  *   segpaged_attention_workspace_size / segpaged_attention_plan
  *                                 once per layout: the work list the attention kernels pop
  *   segpaged_attention            every call: O = attention(Q, paged K/V)
+ * Decode over a layout that grows by one token per step:
+ *   segpaged_build_growable       once: the layout with pages reserved for decode tokens
+ *   segpaged_decode_workspace_size / segpaged_decode_plan
+ *                                 once (re-plan at will): a work list that reads lengths from
+ *                                 the device tables when it runs
+ *   segpaged_append               every step: store each request's new token
+ *   segpaged_decode               every step: O = attention(Q, paged K/V), one query each
  * The dense-plus-mask comparison path (segpaged_dense_mask_*) reads dense K/V directly.
  *
  * Conventions shared by every call
@@ -78,7 +85,8 @@ typedef enum sp_status {
   SP_ERR_POOL_TOO_SMALL = -3,      /* fewer free pages than the layout needs             */
   SP_ERR_WORKSPACE_TOO_SMALL = -4, /* ws_bytes below what the workspace query returned   */
   SP_ERR_HIP = -5,                 /* a HIP runtime call failed                          */
-  SP_ERR_PLAN_MISMATCH = -6        /* workspace holds no plan for these arguments        */
+  SP_ERR_PLAN_MISMATCH = -6,       /* workspace holds no plan for these arguments        */
+  SP_ERR_SEGMENT_FULL = -7         /* segpaged_append: a segment owns no page left       */
 } sp_status;
 
 typedef enum sp_dtype { SP_BF16 = 0, SP_F32 = 1 } sp_dtype;
@@ -160,6 +168,109 @@ sp_status segpaged_build_layers(sp_dtype dtype, int32_t n_layers, int32_t B, int
                                 const int32_t* free_pages, int64_t n_free, int64_t n_phys,
                                 void* k_pool, void* v_pool, int32_t* seg_table, int32_t* kv_len,
                                 int32_t* v2p, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Decode-time growth (page "RedKnot SegPagedAttention runtime design", section 3: LOCAL heads
+ * hold only sink and recent pages, so their storage does not grow with the context; section
+ * 5: layout work is done when KV is written; the product overview page "RedKnot：小红书开源的
+ * 长上下文LLM推理优化工具…", section 3.2, items (1) and (3): LOCAL heads cache a bounded
+ * length of KV and idle pages are reclaimed).
+ *
+ * Growable layout: the segments and page order of segpaged_build for (ctx_len, q_len), but each
+ * segment OWNS enough contiguous virtual pages for reserve[b] more tokens of request b, all
+ * mapped at build (v2p[v] = free_pages[v]); field 3 of a segment row (n_pages above) is the
+ * number of pages it owns. reserve[b] == 0 for all b gives exactly segpaged_build's layout.
+ * Let L be the context, Lmax = L + reserve[b], W the window, S the sink, P the page size:
+ *   GLOBAL            owns ceil(Lmax / P).
+ *   ring              (the recent segment of a LOCAL head: its only segment when S == 0, its
+ *                     second when the head has two) with build pos_start o owns
+ *                     max(ceil((L - o) / P), ceil(min(Lmax - o, W + P - 1) / P)).
+ *   (0, L), S > 0     (sink and window in one segment) owns the largest of ceil(L / P),
+ *                     ceil(min(Lmax, Sp + W - 1) / P) and, if Lmax >= Sp + W,
+ *                     ceil(S / P) + ceil(min(Lmax - Sp, W + P - 1) / P), Sp = ceil(S/P) * P.
+ *   sink segment      owns its pages.
+ * Append (one token per request, at position L = the old context length; the context becomes
+ * L + 1 and the next decode query sits at position L):
+ *   GLOBAL            the token goes to the end of its segment.
+ *   (0, L), S > 0     the token goes to the end of the segment; once the window start
+ *                     L + 1 - W reaches Sp the segment first splits into the sink (0, S) on its
+ *                     first ceil(S / P) pages and a ring starting at Sp on the other pages.
+ *   ring              first its k = floor((L + 1 - W - pos_start) / P) oldest pages (if k > 0)
+ *                     are dropped: pos_start += k*P, n_tok -= k*P, and the segment's v2p
+ *                     entries rotate left by k (the dropped physical pages move to its end,
+ *                     where later tokens reuse them); then the token goes to its end.
+ * A ring thus keeps at most W + P - 1 tokens; fewer than P of them (all older than the window)
+ * are stale, and attention masks them by position. Context-adaptive heads are not growable.
+ * --------------------------------------------------------------------------------------- */
+
+/* Pages (n_virt) and host tables of the growable layout. reserve: host int32 [B] >= 0; a
+ * request with reserve[b] > 0 needs ctx_len[b] >= 1. Errors as segpaged_plan_pages /
+ * segpaged_layout_tables, plus SP_ERR_UNSUPPORTED for SP_LOCAL_ADAPTIVE heads or
+ * ctx_len[b] + reserve[b] >= 2^31. */
+sp_status segpaged_plan_pages_growable(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                                       const int32_t* reserve, int32_t Hkv,
+                                       const sp_head_policy* pol, int32_t page_size,
+                                       int64_t* n_pages_needed);
+sp_status segpaged_layout_tables_growable(int32_t B, const int32_t* ctx_len,
+                                          const int32_t* q_len, const int32_t* reserve,
+                                          int32_t Hkv, const sp_head_policy* pol,
+                                          int32_t page_size, int32_t* seg_table,
+                                          int32_t* kv_len);
+
+/* segpaged_build for the growable layout (same arguments, same errors, plus reserve). The
+ * first build attention call can be segpaged_attention (its segments are segpaged_build's);
+ * after the first segpaged_append only segpaged_decode reads the tables. */
+sp_status segpaged_build_growable(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D,
+                                  int32_t page_size, const int32_t* ctx_len,
+                                  const int32_t* q_len, const int32_t* reserve,
+                                  const sp_head_policy* pol, const void* k_dense,
+                                  const void* v_dense, const int32_t* free_pages, int64_t n_free,
+                                  int64_t n_phys, void* k_pool, void* v_pool,
+                                  int32_t* seg_table, int32_t* kv_len, int32_t* v2p,
+                                  hipStream_t stream);
+
+/* Appends one token to every request with n_new[b] == 1 (n_new: device int32 [B] of 0 / 1, or
+ * NULL for all), following the rules above; one work group per (request, KV head), all state on
+ * the device, nothing read back, no host synchronisation.
+ *   pol          : host [Hkv], SP_GLOBAL or SP_LOCAL (Hkv <= 128)
+ *   k_new, v_new : device [B][Hkv][D], row (b, h) is request b's new token for KV head h
+ *   k_pool, v_pool, n_phys, seg_table, kv_len, v2p : a growable layout (updated in place)
+ *   n_virt       : number of v2p entries (segpaged_plan_pages_growable)
+ *   error        : device int32; the first failing (request, head) writes its code there with
+ *                  an atomic compare-and-swap from 0 (the caller clears it): SP_ERR_SEGMENT_FULL
+ *                  when the token needs a page the segment does not own (appending past the
+ *                  reserve), SP_ERR_INVALID_ARG for an empty head, n_new not 0 or 1, or a page
+ *                  id outside the pool. A failing (request, head) is left unchanged; the others
+ *                  of the launch are appended.
+ * The context length of each request is not passed: it is one past the newest stored token. */
+sp_status segpaged_append(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int32_t page_size,
+                          const sp_head_policy* pol, const int32_t* n_new, const void* k_new,
+                          const void* v_new, void* k_pool, void* v_pool, int64_t n_phys,
+                          int32_t* seg_table, int32_t* kv_len, int32_t* v2p, int64_t n_virt,
+                          int32_t* error, hipStream_t stream);
+
+/* Table-driven decode (page "RedKnot SegPagedAttention runtime design", section 4: each head's
+ * true KV length comes from its page table; section 5: no layout work per call). One query per
+ * request, Q and O [B][Hq][D]; query b sits at request b's newest stored position. The work
+ * list holds (request, KV head, split k of n) items; the kernel takes each head's segments and
+ * lengths from the device seg_table / kv_len when it runs, so one plan serves every decode step
+ * of a growing layout (and any layout segpaged_build writes). ctx_hint (host [B] >= 1, or NULL)
+ * only sizes the KV splits; re-plan when the lengths have drifted far. The workspace, the
+ * combine and reproducibility are as for segpaged_attention; errors likewise, plus
+ * SP_ERR_UNSUPPORTED for SP_LOCAL_ADAPTIVE heads. */
+sp_status segpaged_decode_workspace_size(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                         int32_t D, int32_t page_size, const int32_t* ctx_hint,
+                                         const sp_head_policy* pol, size_t* bytes);
+sp_status segpaged_decode_plan(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                               int32_t page_size, const int32_t* ctx_hint,
+                               const sp_head_policy* pol, void* workspace, size_t ws_bytes,
+                               hipStream_t stream);
+sp_status segpaged_decode(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                          int32_t page_size, const sp_head_policy* pol, const void* q,
+                          const void* k_pool, const void* v_pool, int64_t n_phys,
+                          const int32_t* seg_table, const int32_t* kv_len, const int32_t* v2p,
+                          float softmax_scale, void* o, void* workspace, size_t ws_bytes,
+                          hipStream_t stream);
 
 /* Bytes of device workspace segpaged_attention needs for these arguments (host only). The
  * workspace holds the work list (one item per (request, KV head, query block, KV split),

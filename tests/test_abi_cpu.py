@@ -32,7 +32,7 @@ def test_library_exports_every_declared_call():
 
 
 def test_status_strings():
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         assert sp.status_string(code)
     assert "unknown" in sp.status_string(42)
 
@@ -169,3 +169,55 @@ def test_layers_invalid_arguments():
                                           binding.ctypes.byref(out)) == binding.SP_ERR_INVALID_ARG
     with pytest.raises(sp.SegPagedError):  # second layer's policy invalid
         sp.segpaged_plan_pages_layers([10], [1], [[(1, 4, 64)], [(1, 4, 0)]], 16)
+
+
+def test_growable_layout_tables_match_oracle():
+    # The growable layout (segments own pages for a reserve of decode tokens) from the library's
+    # host code, against the oracle's tables; reserve 0 gives the build layout.
+    from oracle import grow_tables
+    rng = np.random.default_rng(31)
+    for _ in range(300):
+        B, Hkv = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        P = int(rng.choice([16, 32, 64, 128, 256]))
+        ctx = rng.integers(1, 1500, size=B)
+        q = np.array([rng.integers(1, c + 1) if rng.random() < 0.5 else 1 for c in ctx])
+        reserve = rng.integers(0, 2000, size=B) * (rng.random(B) < 0.8)
+        pol = [(0, 0, 1) if rng.random() < 0.3 else
+               (1, int(rng.integers(0, 300)), int(rng.integers(1, 1200))) for _ in range(Hkv)]
+        seg, kvl = sp.segpaged_layout_tables_growable(ctx, q, reserve, pol, P)
+        seg_o, kvl_o, n_virt = grow_tables(ctx, q, reserve, pol, P)
+        np.testing.assert_array_equal(seg, seg_o)
+        np.testing.assert_array_equal(kvl, kvl_o)
+        assert sp.segpaged_plan_pages_growable(ctx, q, reserve, pol, P) == n_virt
+        seg0, _ = sp.segpaged_layout_tables_growable(ctx, q, np.zeros(B), pol, P)
+        np.testing.assert_array_equal(seg0, sp.segpaged_layout_tables(ctx, q, pol, P)[0])
+
+
+def test_growable_and_append_invalid_arguments():
+    with pytest.raises(sp.SegPagedError) as e:  # context-adaptive heads do not grow
+        sp.segpaged_plan_pages_growable([100], [1], [10], [(2, 4, 2)], 64)
+    assert e.value.status == binding.SP_ERR_UNSUPPORTED
+    for ctx, res in (([100], [-1]), ([0], [5])):
+        with pytest.raises(sp.SegPagedError) as e:
+            sp.segpaged_plan_pages_growable(ctx, [0] if ctx == [0] else [1], res,
+                                            [(0, 0, 1)], 64)
+        assert e.value.status == binding.SP_ERR_INVALID_ARG
+    with pytest.raises(sp.SegPagedError) as e:
+        sp.segpaged_plan_pages_growable([2 ** 31 - 10], [1], [100], [(0, 0, 1)], 64)
+    assert e.value.status == binding.SP_ERR_UNSUPPORTED
+    lib = binding.lib()
+    fake = binding._vp(256)
+    pol = np.array([(1, 4, 64)], np.int32)
+    args = lambda p, hkv: (0, 2, hkv, 128, 64, binding._ptr(p), None, fake, fake, fake, fake,
+                           10, fake, fake, fake, 10, fake, None)
+    assert lib.segpaged_append(*args(np.array([(2, 4, 2)], np.int32), 1)) == \
+        binding.SP_ERR_UNSUPPORTED
+    assert lib.segpaged_append(*args(np.array([(1, 4, 0)], np.int32), 1)) == \
+        binding.SP_ERR_INVALID_ARG
+    assert lib.segpaged_append(*args(np.tile(pol, (129, 1)), 129)) == binding.SP_ERR_UNSUPPORTED
+    bad = list(args(pol, 1))
+    bad[7] = None  # k_new
+    assert lib.segpaged_append(*bad) == binding.SP_ERR_INVALID_ARG
+    bad = list(args(pol, 1))
+    bad[15] = 0  # n_virt
+    assert lib.segpaged_append(*bad) == binding.SP_ERR_INVALID_ARG
