@@ -163,6 +163,10 @@ def main() -> int:
                     help="also time one build of N layers of this workload's shape into one "
                          "shared page pool (layer l's KV-head policies are the workload's "
                          "rolled by l heads); reported as build_layers; 0 skips it")
+    ap.add_argument("--decode-steps", type=int, default=0, metavar="N",
+                    help="decode workloads: also time N decode steps over a growable layout, "
+                         "each appending every request's new token (segpaged_append) and then "
+                         "attending (segpaged_decode); reported as decode_append; 0 skips it")
     ap.add_argument("--gemm-reference", action="store_true",
                     help="only time torch's bf16 GEMM (hipBLASLt) at 4096^3..16384^3: what a "
                          "vendor-tuned dense contraction reaches on this GPU, for context")
@@ -178,9 +182,9 @@ def main() -> int:
 
     import torch
 
-    from head_aware_paged_segpaged_amd import (DenseMaskLayer, HipEvent, SegPagedLayer,
-                                               SegPagedLayers)
-    from workloads import config_case, free_list
+    from head_aware_paged_segpaged_amd import (DenseMaskLayer, HipEvent, SegPagedDecoder,
+                                               SegPagedLayer, SegPagedLayers)
+    from workloads import config_case, decode_tokens, free_list
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
@@ -376,6 +380,10 @@ def main() -> int:
                                    % (cpu_nrows, len(sample), case.B * case.Hq, blas_name(),
                                       cpu_s, os.cpu_count() or 0)},
     }
+    if args.decode_steps > 0:
+        line["decode_append"] = decode_append_leg(args, case, k, v, up, evict, stream, ms_step,
+                                                  SegPagedDecoder, HipEvent, decode_tokens,
+                                                  free_list)
     if args.build_layers > 0:
         del layer
         line["build_layers"] = build_layers_leg(args.build_layers, case, k, v, evict, stream,
@@ -389,6 +397,72 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
     return 0
+
+
+def decode_append_leg(args, case, k, v, up, evict, stream, planned_ms, decoder_cls, event_cls,
+                      decode_tokens, free_list) -> dict:
+    """Decode with growth: the workload's context built into a growable layout (pages reserved
+    for the steps to come), then warmup + N steps, each appending every request's new token
+    and running the table-driven decode on it. Timed with HIP events on the stream: the whole
+    loop, and every EVENT_EVERY-th append."""
+    import torch
+    if int(case.q_len.max()) != 1 or (case.policy[:, 0] == 2).any():
+        return {"skipped": "needs a decode workload (one query per request) without "
+                           "context-adaptive heads"}
+    n_steps, n_warm = args.decode_steps, args.warmup
+    total = n_steps + n_warm
+    kn, vn, qn = decode_tokens(case, total)
+    kn, vn, qn = up(kn), up(vn), up(qn)
+    reserve = np.full(case.B, total, dtype=np.int32)
+    dec = decoder_cls(case.dtype, case.Hq, case.Hkv, case.D, case.P, case.ctx_len, case.q_len,
+                      reserve, case.policy, k.device)
+    dec.build(k, v, free_list(case.seed, dec.n_virt))
+    dec.plan()
+    out = torch.empty_like(qn[0])
+    local = case.policy[:, 0] != 0
+
+    def rows():
+        kl = dec.kv_len.cpu().numpy().astype(np.int64)
+        return int(kl[:, local].sum()), int(kl[:, ~local].sum())
+
+    rows0 = rows()
+    for i in range(n_warm):
+        dec.append(kn[i], vn[i])
+        dec.decode(qn[i], case.scale, out=out)
+    torch.cuda.synchronize()
+    rows_w = rows()
+    ev_a = {i: (event_cls(), event_cls()) for i in range(0, n_steps, EVENT_EVERY)}
+    evict()
+    e0, e1 = event_cls(), event_cls()
+    e0.record(stream)
+    for i in range(n_steps):
+        j = n_warm + i
+        ev = ev_a.get(i)
+        if ev:
+            ev[0].record(stream)
+        dec.append(kn[j], vn[j])
+        if ev:
+            ev[1].record(stream)
+        dec.decode(qn[j], case.scale, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_ms(e1) / n_steps
+    append_ms = float(np.mean([a.elapsed_ms(b) for a, b in ev_a.values()]))
+    err = dec.check()
+    assert err == (0, 0), "device-side error %r" % (err,)
+    rows1 = rows()
+    elem = 2 if case.dtype == "bf16" else 4
+    # mean stored rows read per step (GLOBAL heads grow by one row a step)
+    read_rows = (sum(rows_w) + sum(rows1)) / 2.0
+    step_bytes = (2.0 * read_rows * case.D * elem + 2.0 * case.B * case.Hq * case.D * elem
+                  + 2.0 * 2.0 * case.B * case.Hkv * case.D * elem)  # + the appended rows
+    gbps = step_bytes / ((ms - append_ms) * 1e-3) / 1e9
+    return {"steps": n_steps, "warmup": n_warm, "ms_per_step": round(ms, 5),
+            "append_ms": round(append_ms, 5), "tokens_per_s": round(case.B / (ms * 1e-3), 1),
+            "decode_gbps": round(gbps, 1), "decode_hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "vs_planned_step": round(ms / planned_ms, 3),
+            "local_rows": [rows0[0], rows1[0]], "global_rows": [rows0[1], rows1[1]],
+            "pages_owned": int(dec.n_virt)}
 
 
 def build_layers_leg(n_layers, case, k, v, evict, stream, layers_cls, event_cls,

@@ -199,3 +199,48 @@ def test_append_past_the_reserve_reports_segment_full():
             after = dec.seg_table.cpu().numpy()
             np.testing.assert_array_equal(after[0, 0], before[0, 0])
             assert after[0, 1, 0, 1] + after[0, 1, 1, 1] > 0
+
+
+@pytest.mark.parametrize("index", [3, 5])
+def test_full_size_decode_append_sampled(index):
+    # The full decode workload (64 requests, 4K-128K contexts, or its 32K+ slice) built into a
+    # growable layout, then 16 decode steps, each appending a token per request: tables
+    # bit-exact against the append oracle after every step, and seeded sampled rows of the
+    # last step's output against the dense oracle over the grown contexts.
+    from workloads import config_case, decode_tokens
+    c = config_case(index)
+    n = 16
+    print("case full-size append", c.name, flush=True)
+    kn, vn, qn = decode_tokens(c, n)
+    reserve = np.full(c.B, n)
+    dec = SegPagedDecoder(c.dtype, c.Hq, c.Hkv, c.D, c.P, c.ctx_len, c.q_len, reserve, c.policy,
+                          DEV)
+    dec.build(to_device(c.k, c.dtype), to_device(c.v, c.dtype), free_list(c.seed, dec.n_virt))
+    st, kl, nv = oracle.grow_tables(c.ctx_len, c.q_len, reserve, c.policy, c.P)
+    v2p = free_list(c.seed, nv)
+    dec.plan()
+    kd, vd, qd = to_device(kn, c.dtype), to_device(vn, c.dtype), to_device(qn, c.dtype)
+    for i in range(n):
+        dec.append(kd[i], vd[i])
+        out = dec.decode(qd[i], c.scale)
+        st, kl, v2p, _ = oracle.append_step(st, kl, v2p, c.policy, c.P)
+        np.testing.assert_array_equal(dec.seg_table.cpu().numpy(), st)
+        np.testing.assert_array_equal(dec.kv_len.cpu().numpy(), kl)
+    np.testing.assert_array_equal(dec.v2p.cpu().numpy(), v2p)
+    assert dec.check() == (0, 0)
+    got = to_f64(out)
+    rng = np.random.default_rng(100 + index)
+    worst_abs, worst_cos = 0.0, 1.0
+    for _ in range(12):
+        b, hq = int(rng.integers(c.B)), int(rng.integers(c.Hq))
+        kv0, L = int(c.ctx_len[:b].sum()), int(c.ctx_len[b])
+        k_b = np.concatenate([c.k[kv0:kv0 + L], kn[:, b]])
+        v_b = np.concatenate([c.v[kv0:kv0 + L], vn[:, b]])
+        ref = oracle.attention_rows(qn[n - 1, b][None], k_b, v_b, [L + n], [1], c.policy, c.Hq,
+                                    c.Hkv, c.scale, c.dtype, 0, hq)[0]
+        g = got[b, hq]
+        worst_abs = max(worst_abs, float(np.abs(g - ref).max()))
+        worst_cos = min(worst_cos, float(g @ ref / (np.linalg.norm(g) * np.linalg.norm(ref))))
+    print("%s append sampled: maxabs=%.3e min_cos=%.8f" % (c.name, worst_abs, worst_cos),
+          flush=True)
+    assert worst_abs <= MAXABS[c.dtype] and worst_cos > COS_MIN

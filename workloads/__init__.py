@@ -13,5 +13,6 @@ from .synth import (  # noqa: F401
     Case,
     config_case,
     custom_case,
+    decode_tokens,
     free_list,
 )

@@ -212,6 +212,20 @@ def _attach_tensors(case: Case, q_std: float, kv_std: float) -> None:
     case.v = _draw_tensor(case.seed, 3, (case.t_total, case.Hkv, case.D), kv_std, case.dtype)
 
 
+def decode_tokens(case: Case, n_steps: int, q_std: float | None = None,
+                  kv_std: float = 1.0):
+    """Seeded inputs of n_steps decode steps after ``case``'s context: the new token's K and V
+    rows [n_steps, B, Hkv, D] and the step's queries [n_steps, B, Hq, D] (same dtype and
+    distributions as the workload's own tensors; tensor ids 5-7 of the case's seed)."""
+    if q_std is None:
+        q_std = 1.0 / math.sqrt(128) if case.dtype == "bf16" else 1.0
+    kv_shape = (n_steps, case.B, case.Hkv, case.D)
+    k = _draw_tensor(case.seed, 5, kv_shape, kv_std, case.dtype)
+    v = _draw_tensor(case.seed, 6, kv_shape, kv_std, case.dtype)
+    q = _draw_tensor(case.seed, 7, (n_steps, case.B, case.Hq, case.D), q_std, case.dtype)
+    return k, v, q
+
+
 def free_list(seed: int, n_phys: int) -> np.ndarray:
     """Seeded permutation of the physical page ids ``0 .. n_phys-1`` (int32)."""
     g = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(4,)))
