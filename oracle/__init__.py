@@ -14,7 +14,10 @@ What it computes, and from which passage of the RedKnot pages:
   tokens (same page, sections 1-3; page "RedKnot head classification", the four head types,
   defaults window 512 and sink 4). So the oracle is that definition written out. An adaptive
   LOCAL head has window max(1, L // d) for a request of context length L (page "RedKnot head
-  classification", windows that scale with the request's context).
+  classification", windows that scale with the request's context). A RETRIEVAL head sees the
+  top fraction of its prefix tokens by an importance input, its sink and its query chunk
+  (same page, the four head types; page "RedKnot SegPagedAttention runtime design", closing
+  summary: retrieval heads take pages on demand).
 * ``plan``: the per-(request, KV head) segment list, true KV length, virtual page ids and the
   virtual-to-physical map (page "RedKnot SegPagedAttention runtime design", section 3: one
   page table per (layer, head, segment) over contiguous virtual pages, a shared physical
@@ -32,6 +35,6 @@ example). Nothing here is "parity unpinned".
 """
 
 from .attention import GLOBAL, LOCAL, attention, attention_rows, to_f64, visible  # noqa: F401
-from .plan import (LOCAL_ADAPTIVE, gather_positions, head_policy, plan_tables,  # noqa: F401
-                   plan_tables_layers, segments)
+from .plan import (LOCAL_ADAPTIVE, RETRIEVAL, gather_positions, head_policy,  # noqa: F401
+                   plan_tables, plan_tables_layers, retrieval_counts, retrieval_keep, segments)
 from .append import append_step, grow_tables, owned_pages  # noqa: F401

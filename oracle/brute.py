@@ -38,3 +38,34 @@ def attention_row(q_row, k_rows, v_rows, p: int, kind: int, sink: int, window: i
         for c in range(d):
             out[c] += (wi / tot) * v_rows[j][c]
     return out
+
+
+def retrieval_kept(importance, sink: int, permille: int, prefix: int):
+    """Kept prefix positions of a RETRIEVAL head, found by repeatedly taking the most important
+    token not yet taken (scanning positions upward, so a tie goes to the lower position)."""
+    first = list(range(min(sink, prefix)))
+    rest = list(range(len(first), prefix))
+    k = (permille * len(rest) + 999) // 1000
+    chosen = []
+    for _ in range(k):
+        best = None
+        for j in rest:
+            if j in chosen:
+                continue
+            if best is None or importance[j] > importance[best]:
+                best = j
+        chosen.append(best)
+    return sorted(first + chosen)
+
+
+def attention_row_over(q_row, k_rows, v_rows, vis, scale: float):
+    """One output row over an explicit list of visible key positions."""
+    logits = [scale * sum(a * c for a, c in zip(q_row, k_rows[j])) for j in vis]
+    mx = max(logits)
+    w = [math.exp(x - mx) for x in logits]
+    tot = sum(w)
+    out = [0.0] * len(v_rows[0])
+    for wi, j in zip(w, vis):
+        for c in range(len(out)):
+            out[c] += (wi / tot) * v_rows[j][c]
+    return out

@@ -30,6 +30,17 @@ Readings taken where the pages are silent (one layer per call):
   scale with each request's context length, whose example is half the context) is a LOCAL
   head whose window for a request of context length L is max(1, L // d), d being its
   configured divisor; L is the request's whole context at this call, query chunk included.
+* A RETRIEVAL head (page "RedKnot head classification", the four head types: full KV of which
+  only the top-p important tokens are kept; page "RedKnot SegPagedAttention runtime design",
+  closing summary: retrieval heads take only the pages they need) with sink S and keep fraction
+  p = window / 1000 keeps, of the prefix before the query chunk (positions < L - q): its first
+  min(S, L - q) tokens, and of the others the ceil(p * n) with the highest importance (n =
+  their count; importance is an input, one float per (token, KV head); ties go to the lower
+  position). It also keeps the whole chunk, which its own queries see causally. Segments: the
+  kept prefix tokens compacted in position order (slot i of the segment holds the i-th kept
+  position; pos_start reads 0), then the chunk (L - q, q); a head with an empty prefix has the
+  chunk alone. The count of kept tokens depends only on (L, q, S, p), so the tables do too;
+  which tokens fill the first segment depends on the importance.
 """
 
 from __future__ import annotations
@@ -39,6 +50,7 @@ import numpy as np
 GLOBAL = 0
 LOCAL = 1
 LOCAL_ADAPTIVE = 2
+RETRIEVAL = 3
 
 
 def head_policy(kind: int, sink: int, window: int, L: int):
@@ -49,12 +61,32 @@ def head_policy(kind: int, sink: int, window: int, L: int):
     return kind, sink, window
 
 
+def retrieval_counts(sink: int, permille: int, L: int, q: int):
+    """(sink tokens kept, other prefix tokens kept) of a RETRIEVAL head."""
+    prefix = max(0, L - q)
+    s = min(sink, prefix)
+    n = prefix - s
+    return s, -(-permille * n // 1000)
+
+
+def retrieval_keep(importance, sink: int, permille: int, L: int, q: int):
+    """Kept prefix positions of a RETRIEVAL head, ascending. importance[j] for j < L - q."""
+    s, k = retrieval_counts(sink, permille, L, q)
+    prefix = max(0, L - q)
+    others = sorted(range(s, prefix), key=lambda j: (-float(importance[j]), j))
+    return sorted(list(range(s)) + others[:k])
+
+
 def segments(kind: int, sink: int, window: int, L: int, q: int):
     """List of (pos_start, n_tok) for one (request, KV head)."""
     if L <= 0:
         return []
     if kind == GLOBAL:
         return [(0, L)]
+    if kind == RETRIEVAL:
+        s, k = retrieval_counts(sink, window, L, q)
+        segs = [(0, s + k)] if s + k > 0 else []
+        return segs + ([(L - q, q)] if q > 0 else [])
     if kind != LOCAL:
         raise ValueError(kind)
     s = min(sink, L)
@@ -120,12 +152,14 @@ def plan_tables_layers(ctx_len, q_len, policies, P: int):
     return seg_table, kv_len, v
 
 
-def gather_positions(seg_table, v2p, P: int, b: int, h: int):
-    """(position, physical page, slot) of every token stored for (b, h), in position order."""
+def gather_positions(seg_table, v2p, P: int, b: int, h: int, kept=None):
+    """(position, physical page, slot) of every token stored for (b, h), in position order.
+    ``kept``: the kept prefix positions of a RETRIEVAL head, whose first segment holds them."""
     out = []
     for s in range(2):
         pos, n, vstart, npg = (int(x) for x in seg_table[b, h, s])
         for i in range(n):
             vpage = vstart + i // P
-            out.append((pos + i, int(v2p[vpage]), i % P))
+            p = int(kept[i]) if (s == 0 and kept is not None and len(kept)) else pos + i
+            out.append((p, int(v2p[vpage]), i % P))
     return out

@@ -10,9 +10,11 @@ from .synth import (  # noqa: F401
     GLOBAL,
     LOCAL,
     LOCAL_ADAPTIVE,
+    RETRIEVAL,
     Case,
     config_case,
     custom_case,
     decode_tokens,
     free_list,
+    importance_scores,
 )

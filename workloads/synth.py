@@ -36,6 +36,7 @@ import numpy as np
 GLOBAL = 0
 LOCAL = 1
 LOCAL_ADAPTIVE = 2  # LOCAL with window = context length // divisor
+RETRIEVAL = 3  # top fraction (window / 1000) of the prefix by importance, sink and chunk
 
 CHUNK = 1 << 22
 
@@ -224,6 +225,17 @@ def decode_tokens(case: Case, n_steps: int, q_std: float | None = None,
     v = _draw_tensor(case.seed, 6, kv_shape, kv_std, case.dtype)
     q = _draw_tensor(case.seed, 7, (n_steps, case.B, case.Hq, case.D), q_std, case.dtype)
     return k, v, q
+
+
+def importance_scores(case: Case, levels: int = 0) -> np.ndarray:
+    """Seeded per-(token, KV head) importance, float32 [sum(ctx_len), Hkv], for RETRIEVAL
+    heads: exp of a standard normal (a heavy right tail: a few tokens matter much more than the
+    rest). levels > 0 rounds the draws to that many distinct values, so that ties occur."""
+    x = _fill_normal(case.seed, 8, case.t_total * case.Hkv, 1.0)
+    if levels > 0:
+        x = np.floor((np.clip(x, -3.0, 3.0) + 3.0) / 6.0 * (levels - 1) + 0.5).astype(np.float32)
+        return x.reshape(case.t_total, case.Hkv)
+    return np.exp(x).astype(np.float32).reshape(case.t_total, case.Hkv)
 
 
 def free_list(seed: int, n_phys: int) -> np.ndarray:
