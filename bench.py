@@ -40,6 +40,13 @@ def head_window(kind: int, window: int, L: int) -> int:
     return max(1, L // window) if kind == 2 else window
 
 
+def retrieval_kept(S: int, permille: int, L: int, nq: int) -> int:
+    """Prefix tokens a RETRIEVAL head keeps (its sink and the top fraction of the rest)."""
+    prefix = max(0, L - nq)
+    s = min(S, prefix)
+    return s + -(-permille * (prefix - s) // 1000)
+
+
 def visible_counts(case) -> np.ndarray:
     """Visible (query, key) pairs per (request, KV head), one query head's worth."""
     out = np.zeros((case.B, case.Hkv), dtype=np.float64)
@@ -51,6 +58,8 @@ def visible_counts(case) -> np.ndarray:
             W = head_window(kind, W, L)
             if kind == 0:
                 n = p + 1
+            elif kind == 3:
+                n = retrieval_kept(S, W, L, nq) + (p - (L - nq) + 1)
             else:
                 lo = np.maximum(0, p - W + 1)
                 n = (p - lo + 1) + np.minimum(S, lo)
@@ -93,7 +102,7 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_oracle_sample(case, budget_rows: int):
+def cpu_oracle_sample(case, budget_rows: int, importance=None):
     """Times the fp64 oracle on a bounded sample of (request, query head) rows."""
     import oracle
 
@@ -117,7 +126,8 @@ def cpu_oracle_sample(case, budget_rows: int):
         rows += len(toks)
     t0 = time.perf_counter()
     outs = [oracle.attention_rows(case.q, case.k, case.v, case.ctx_len, case.q_len, case.policy,
-                                  case.Hq, case.Hkv, case.scale, case.dtype, b, hq, toks)
+                                  case.Hq, case.Hkv, case.scale, case.dtype, b, hq, toks,
+                                  importance=importance)
             for b, hq, toks in sample]
     secs = time.perf_counter() - t0
     # visible pairs of the sample
@@ -130,6 +140,8 @@ def cpu_oracle_sample(case, budget_rows: int):
         W = head_window(kind, W, L)
         if kind == 0:
             pairs += float((p + 1).sum())
+        elif kind == 3:
+            pairs += float((retrieval_kept(S, W, L, nq) + (p - (L - nq) + 1)).sum())
         else:
             lo = np.maximum(0, p - W + 1)
             pairs += float(((p - lo + 1) + np.minimum(S, lo)).sum())
@@ -142,8 +154,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=1,
-                    help="workload index (0-6; 5 = the 32K-128K slice of the decode workload, "
-                         "6 = the decode workload with context-adaptive LOCAL windows); "
+                    help="workload index (0-7; 5 = the 32K-128K slice of the decode workload, "
+                         "6 = the decode workload with context-adaptive LOCAL windows, "
+                         "7 = the decode workload with two RETRIEVAL heads); "
                          "default 1")
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="rows of the CPU-oracle sample (default sized for about 10-30 s)")
@@ -184,7 +197,7 @@ def main() -> int:
 
     from head_aware_paged_segpaged_amd import (DenseMaskLayer, HipEvent, SegPagedDecoder,
                                                SegPagedLayer, SegPagedLayers)
-    from workloads import config_case, decode_tokens, free_list
+    from workloads import config_case, decode_tokens, free_list, importance_scores
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
@@ -208,7 +221,9 @@ def main() -> int:
     # Build: allocated once, then timed separately, with cold caches, as the median of a few
     # rebuilds into the same buffers: the library call (host checks, table upload, scatter
     # kernels) on wall clock, and on HIP events around it on the stream.
-    layer.build(k, v, fl)
+    # RETRIEVAL heads keep the top fraction of their prefix by a seeded importance input
+    importance = importance_scores(case) if (case.policy[:, 0] == 3).any() else None
+    layer.build(k, v, fl, importance=importance)
     # Cache eviction between timed runs: READ a 512 MiB buffer that is never written. A
     # written buffer would leave dirty lines in the L2s and the MALL whose write-back then
     # lands inside the timed kernel (measured: a plain read kernel loses 11 % that way).
@@ -301,7 +316,9 @@ def main() -> int:
 
     # Dense + mask baseline on the same inputs.
     dense = None
-    if not args.no_dense:
+    if importance is not None and not args.no_dense:
+        dense = {"skipped": "the dense-plus-mask path has no mask for RETRIEVAL heads"}
+    elif not args.no_dense:
         dl = DenseMaskLayer(case.dtype, case.Hq, case.Hkv, case.D, case.ctx_len, case.q_len,
                             case.policy, dev)
         dl.plan()
@@ -325,7 +342,7 @@ def main() -> int:
         # the oracle converts one whole (request, KV head) to fp64 per sampled row set, so
         # decode rows (one per head, contexts up to 128K) are far dearer than prefill rows
         args.cpu_rows = 256 if int(case.q_len.max()) == 1 else 16384
-    sample, ref_rows, cpu_s, cpu_pairs, cpu_nrows = cpu_oracle_sample(case, args.cpu_rows)
+    sample, ref_rows, cpu_s, cpu_pairs, cpu_nrows = cpu_oracle_sample(case, args.cpu_rows, importance)
     got = out.float().cpu().numpy().astype(np.float64)
     q_row0 = np.concatenate([[0], np.cumsum(case.q_len)[:-1]])
     maxabs, cos_min = 0.0, 1.0
@@ -360,14 +377,16 @@ def main() -> int:
                                          int(case.policy[:, 2].max())],
                    "local_window_rule": ("context length // %d" % int(case.policy[:, 2].max())
                                          if (case.policy[:, 0] == 2).any() else "fixed"),
-                   "gqa_group": G},
+                   "gqa_group": G,
+                   "retrieval_kv_heads": [[int(h), int(case.policy[h, 2])] for h in
+                                          np.nonzero(case.policy[:, 0] == 3)[0]]},
         "gbps": round(gbps, 1),
         "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
         "visible_tflop_per_step": round(flops / 1e12, 6),
         "roofline": roof,
         "cold_cache": cold,
         "dense_mask": dense,
-        "speedup_vs_dense_mask": dense["speedup"] if dense else None,
+        "speedup_vs_dense_mask": dense.get("speedup") if dense else None,
         "build": {"runs": BUILD_RUNS, "seconds": round(build_s, 6),
                   "stream_ms": round(build_ms, 4), "bytes": build_bytes, "gbps_wall": round(build_bytes / build_s / 1e9, 1),
                   "gbps_stream": round(build_bytes / (build_ms * 1e-3) / 1e9, 1)},
@@ -406,9 +425,9 @@ def decode_append_leg(args, case, k, v, up, evict, stream, planned_ms, decoder_c
     and running the table-driven decode on it. Timed with HIP events on the stream: the whole
     loop, and every EVENT_EVERY-th append."""
     import torch
-    if int(case.q_len.max()) != 1 or (case.policy[:, 0] == 2).any():
+    if int(case.q_len.max()) != 1 or (case.policy[:, 0] >= 2).any():
         return {"skipped": "needs a decode workload (one query per request) without "
-                           "context-adaptive heads"}
+                           "context-adaptive or retrieval heads"}
     n_steps, n_warm = args.decode_steps, args.warmup
     total = n_steps + n_warm
     kn, vn, qn = decode_tokens(case, total)

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     SP_GLOBAL,
     SP_LOCAL,
     SP_LOCAL_ADAPTIVE,
+    SP_RETRIEVAL,
     HipEvent,
     SegPagedError,
     lib,
@@ -25,6 +26,7 @@ from .binding import (  # noqa: F401
     segpaged_build,
     segpaged_build_growable,
     segpaged_build_layers,
+    segpaged_build_scored,
     segpaged_decode,
     segpaged_decode_plan,
     segpaged_decode_workspace_size,
@@ -36,6 +38,7 @@ from .binding import (  # noqa: F401
     segpaged_layout_tables_layers,
     segpaged_plan_pages,
     segpaged_plan_pages_growable,
+    segpaged_retrieval_rows,
     segpaged_plan_pages_layers,
     status_string,
 )

@@ -70,7 +70,8 @@ def build(verbose: bool = False) -> str:
             if verbose and err.strip():
                 print(err, file=sys.stderr)
         tmp = LIB + ".tmp%d" % os.getpid()
-        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp],
+             verbose)
     os.replace(tmp, LIB)
     return LIB
 

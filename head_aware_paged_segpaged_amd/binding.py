@@ -31,6 +31,7 @@ SP_F32 = 1
 SP_GLOBAL = 0
 SP_LOCAL = 1
 SP_LOCAL_ADAPTIVE = 2
+SP_RETRIEVAL = 3
 
 EXPORTED = [
     "segpaged_status_string",
@@ -40,6 +41,8 @@ EXPORTED = [
     "segpaged_layout_tables_layers",
     "segpaged_build",
     "segpaged_build_layers",
+    "segpaged_retrieval_rows",
+    "segpaged_build_scored",
     "segpaged_plan_pages_growable",
     "segpaged_layout_tables_growable",
     "segpaged_build_growable",
@@ -82,6 +85,9 @@ _SIGS = {
                                      _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "segpaged_build": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                               _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "segpaged_retrieval_rows": (_i32, [_i32, _vp, _vp, _i32, _vp, ctypes.POINTER(_i64)]),
+    "segpaged_build_scored": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "segpaged_plan_pages_growable": (_i32, [_i32, _vp, _vp, _vp, _i32, _vp, _i32,
                                             ctypes.POINTER(_i64)]),
     "segpaged_layout_tables_growable": (_i32, [_i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp]),
@@ -249,6 +255,31 @@ def segpaged_build_layers(dtype, D: int, page_size: int, ctx_len, q_len, policy,
                                        _dev(v_pool, "v_pool"), _dev(seg_table, "seg_table"),
                                        _dev(kv_len, "kv_len"), _dev(v2p, "v2p"),
                                        _stream(stream)), "segpaged_build_layers")
+
+
+def segpaged_retrieval_rows(ctx_len, q_len, policy) -> int:
+    c, q, p = _host_i32(ctx_len), _host_i32(q_len), _host_i32(policy).reshape(-1, 3)
+    out = _i64(0)
+    _check(lib().segpaged_retrieval_rows(len(c), _ptr(c), _ptr(q), p.shape[0], _ptr(p),
+                                         ctypes.byref(out)), "segpaged_retrieval_rows")
+    return int(out.value)
+
+
+def segpaged_build_scored(dtype, D: int, page_size: int, ctx_len, q_len, policy, importance,
+                          k_dense, v_dense, free_pages, n_phys: int, k_pool, v_pool, seg_table,
+                          kv_len, v2p, row_pos, stream=None) -> None:
+    """importance: host float32 [sum(ctx_len)][Hkv]; row_pos: device int32 (or None)."""
+    c, q, p = _host_i32(ctx_len), _host_i32(q_len), _host_i32(policy).reshape(-1, 3)
+    fl = _host_i32(free_pages)
+    imp = np.ascontiguousarray(np.asarray(importance, dtype=np.float32))
+    _check(lib().segpaged_build_scored(_dtype_code(dtype), len(c), p.shape[0], D, page_size,
+                                       _ptr(c), _ptr(q), _ptr(p), _ptr(imp),
+                                       _dev(k_dense, "k_dense"), _dev(v_dense, "v_dense"),
+                                       _ptr(fl), fl.size, n_phys, _dev(k_pool, "k_pool"),
+                                       _dev(v_pool, "v_pool"), _dev(seg_table, "seg_table"),
+                                       _dev(kv_len, "kv_len"), _dev(v2p, "v2p"),
+                                       _dev(row_pos, "row_pos"), _stream(stream)),
+           "segpaged_build_scored")
 
 
 def segpaged_plan_pages_growable(ctx_len, q_len, reserve, policy, page_size: int) -> int:

@@ -2,8 +2,12 @@
 // and kernel launches. Every argument is checked before anything is queued.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <functional>
+#include <thread>
 #include <vector>
 
 #include "launch.h"
@@ -173,12 +177,83 @@ sp_status layout_impl(int32_t n_layers, int32_t B, const int32_t* ctx_len, const
 }
 
 // Build of n_layers layers (growable when `reserve` is not null: single layer only).
+// Kept positions of every RETRIEVAL head of a single-layer layout, in (request, head) order:
+// the sink, then the top fraction of the other prefix tokens by importance (ties: lower
+// position), ascending. offsets[b * Hkv + h] = start of (b, h) in the list (-1: none). Heads
+// are independent and are shared out over host threads.
+sp_status retrieval_keep_lists(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                               int32_t Hkv, const sp_head_policy* pol, const float* importance,
+                               std::vector<int32_t>* pos, std::vector<int64_t>* offsets) {
+  struct Task {
+    int64_t row0, out;
+    int32_t h, s, k, prefix;
+  };
+  std::vector<Task> tasks;
+  offsets->assign(size_t(B) * Hkv, -1);
+  int64_t row0 = 0, total = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    for (int32_t h = 0; h < Hkv; ++h) {
+      if (pol[h].kind != SP_RETRIEVAL) continue;
+      int32_t s = 0, k = 0;
+      retrieval_counts(pol[h], ctx_len[b], q_len[b], &s, &k);
+      if (s + k == 0) continue;
+      if (importance == nullptr) return SP_ERR_INVALID_ARG;
+      (*offsets)[size_t(b) * Hkv + h] = total;
+      tasks.push_back(Task{row0, total, h, s, k, ctx_len[b] - q_len[b]});
+      total += s + k;
+    }
+    row0 += ctx_len[b];
+  }
+  pos->assign(size_t(total), 0);
+  // longest heads first, so the threads finish together
+  std::stable_sort(tasks.begin(), tasks.end(),
+                   [](const Task& a, const Task& c) { return a.prefix > c.prefix; });
+  std::atomic<bool> bad{false};
+  std::atomic<size_t> next{0};
+  // Per head: the k-th largest importance t (a selection on a contiguous copy), then one pass
+  // in position order that takes every token above t and the lowest-positioned ones equal to
+  // t until k are taken, so the list comes out ascending.
+  auto work = [&]() {
+    std::vector<float> col, sel;
+    for (size_t t = next++; t < tasks.size(); t = next++) {
+      const Task& tk = tasks[t];
+      int32_t* out = pos->data() + tk.out;
+      for (int32_t j = 0; j < tk.s; ++j) out[j] = j;
+      const int32_t n = tk.prefix - tk.s;
+      col.resize(size_t(n));
+      for (int32_t j = 0; j < n; ++j) {
+        col[size_t(j)] = importance[(tk.row0 + tk.s + j) * Hkv + tk.h];
+        if (!std::isfinite(col[size_t(j)])) bad = true;
+      }
+      if (tk.k == 0) continue;
+      sel = col;
+      std::nth_element(sel.begin(), sel.begin() + (tk.k - 1), sel.end(), std::greater<float>());
+      const float thr = sel[size_t(tk.k - 1)];
+      int32_t above = 0;
+      for (float v : col) above += v > thr;
+      int32_t ties = tk.k - above, w = tk.s;
+      for (int32_t j = 0; j < n; ++j) {
+        const float v = col[size_t(j)];
+        if (v > thr || (v == thr && ties-- > 0)) out[w++] = tk.s + j;
+      }
+    }
+  };
+  const int n_threads = int(std::min<size_t>(
+      tasks.size(), size_t(std::max(1u, std::min(16u, std::thread::hardware_concurrency())))));
+  std::vector<std::thread> pool;
+  for (int i = 1; i < n_threads; ++i) pool.emplace_back(work);
+  work();
+  for (std::thread& th : pool) th.join();
+  return bad ? SP_ERR_INVALID_ARG : SP_OK;
+}
+
 sp_status build_impl(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv, int32_t D,
                      int32_t page_size, const int32_t* ctx_len, const int32_t* q_len,
                      const int32_t* reserve, const sp_head_policy* pol, const void* k_dense,
                      const void* v_dense, const int32_t* free_pages, int64_t n_free,
                      int64_t n_phys, void* k_pool, void* v_pool, int32_t* seg_table,
-                     int32_t* kv_len, int32_t* v2p, hipStream_t stream) {
+                     int32_t* kv_len, int32_t* v2p, hipStream_t stream,
+                     const float* importance = nullptr, int32_t* row_pos = nullptr) {
   sp_status st = check_dtype_dim(dtype, D);
   if (st != SP_OK) return st;
   if (n_free < 0 || n_phys < 0) return SP_ERR_INVALID_ARG;
@@ -190,6 +265,16 @@ sp_status build_impl(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv, i
   if (int64_t(n_layers) * t_total > 0x7fffffffLL) return SP_ERR_UNSUPPORTED;  // int32 rows
   if (B == 0) return SP_OK;
   if (seg_table == nullptr || kv_len == nullptr) return SP_ERR_INVALID_ARG;
+  std::vector<int32_t> keep;
+  std::vector<int64_t> keep_off;
+  bool retrieval = false;
+  for (size_t i = 0; i < size_t(n_layers) * Hkv; ++i) retrieval |= pol[i].kind == SP_RETRIEVAL;
+  if (retrieval) {
+    if (n_layers != 1) return SP_ERR_INVALID_ARG;
+    st = retrieval_keep_lists(B, ctx_len, q_len, Hkv, pol, importance, &keep, &keep_off);
+    if (st != SP_OK) return st;
+    if (!keep.empty() && row_pos == nullptr) return SP_ERR_INVALID_ARG;
+  }
   const int64_t n_virt = lay.n_virt;
   if (n_free < n_virt) return SP_ERR_POOL_TOO_SMALL;
   if (n_virt > 0) {
@@ -226,6 +311,9 @@ sp_status build_impl(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv, i
                                      hipMemcpyHostToDevice, stream) != hipSuccess)
       return SP_ERR_HIP;
   }
+  if (!keep.empty() && hipMemcpyAsync(row_pos, keep.data(), keep.size() * 4,
+                                      hipMemcpyHostToDevice, stream) != hipSuccess)
+    return SP_ERR_HIP;
   if (hipStreamSynchronize(stream) != hipSuccess) return SP_ERR_HIP;
 
   // Scatter: one launch per run of at most kMaxBuildSegs non-empty segments, over all layers.
@@ -236,6 +324,7 @@ sp_status build_impl(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv, i
   bp.kp = k_pool;
   bp.vp = v_pool;
   bp.v2p = v2p;
+  bp.row_pos = row_pos;
   bp.Hkv = Hkv;
   bp.P = page_size;
   auto flush = [&]() -> sp_status {
@@ -258,11 +347,13 @@ sp_status build_impl(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv, i
             if (st != SP_OK) return st;
           }
           BuildSeg& e = bp.seg[bp.nseg++];
+          const bool gather = s == 0 && !keep_off.empty() && keep_off[size_t(b) * Hkv + h] >= 0;
           e.chunk0 = bp.nchunks;
-          e.src_row0 = int32_t(row0 + sg.pos);
+          e.src_row0 = int32_t(row0 + (gather ? 0 : sg.pos));
           e.vstart = sg.vstart;
           e.ntok = sg.ntok;
           e.h = h;
+          e.pos_off = gather ? int32_t(keep_off[size_t(b) * Hkv + h]) : -1;
           bp.nchunks += (sg.ntok + kChunk - 1) / kChunk;
         }
       }
@@ -354,6 +445,36 @@ sp_status segpaged_layout_tables_layers(int32_t n_layers, int32_t B, const int32
   if (st != SP_OK) return st;
   layout_tables(lay, n_layers * B * Hkv, seg_table, kv_len);
   return SP_OK;
+}
+
+sp_status segpaged_retrieval_rows(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                                  int32_t Hkv, const sp_head_policy* pol, int64_t* n_rows) {
+  if (n_rows == nullptr) return SP_ERR_INVALID_ARG;
+  sp_status st = check_lengths_policy(B, ctx_len, q_len, Hkv, pol);
+  if (st != SP_OK) return st;
+  int64_t n = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    for (int32_t h = 0; h < Hkv; ++h) {
+      if (pol[h].kind != SP_RETRIEVAL) continue;
+      int32_t s = 0, k = 0;
+      retrieval_counts(pol[h], ctx_len[b], q_len[b], &s, &k);
+      n += s + k;
+    }
+  }
+  *n_rows = n;
+  return SP_OK;
+}
+
+sp_status segpaged_build_scored(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D,
+                                int32_t page_size, const int32_t* ctx_len, const int32_t* q_len,
+                                const sp_head_policy* pol, const float* importance,
+                                const void* k_dense, const void* v_dense,
+                                const int32_t* free_pages, int64_t n_free, int64_t n_phys,
+                                void* k_pool, void* v_pool, int32_t* seg_table, int32_t* kv_len,
+                                int32_t* v2p, int32_t* row_pos, hipStream_t stream) {
+  return build_impl(dtype, 1, B, Hkv, D, page_size, ctx_len, q_len, nullptr, pol, k_dense,
+                    v_dense, free_pages, n_free, n_phys, k_pool, v_pool, seg_table, kv_len, v2p,
+                    stream, importance, row_pos);
 }
 
 sp_status segpaged_plan_pages_growable(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
@@ -625,7 +746,8 @@ sp_status segpaged_append(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int
   if (B < 0 || Hkv < 1 || pol == nullptr) return SP_ERR_INVALID_ARG;
   if (Hkv > kMaxAppendHeads) return SP_ERR_UNSUPPORTED;
   for (int32_t h = 0; h < Hkv; ++h) {
-    if (pol[h].kind == SP_LOCAL_ADAPTIVE) return SP_ERR_UNSUPPORTED;
+    if (pol[h].kind == SP_LOCAL_ADAPTIVE || pol[h].kind == SP_RETRIEVAL)
+      return SP_ERR_UNSUPPORTED;
     if (pol[h].kind != SP_GLOBAL && pol[h].kind != SP_LOCAL) return SP_ERR_INVALID_ARG;
     if (pol[h].kind == SP_LOCAL && (pol[h].sink < 0 || pol[h].window < 1))
       return SP_ERR_INVALID_ARG;

@@ -1283,7 +1283,8 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnParams p) {
 
 // ---------------------------------------------------------------------------------------
 // Build / scatter: one work group copies 64 stored tokens (K and V) of one segment from the
-// dense [T][Hkv][D] tensors into their pool pages. Reads are whole D-rows, writes are whole
+// dense [T][Hkv][D] tensors into their pool pages (a RETRIEVAL head's kept-prefix segment takes
+// its tokens' positions from a list: a gather). Reads are whole D-rows, writes are whole
 // contiguous page rows; both are streaming (non-temporal) accesses, each byte is touched once.
 // ---------------------------------------------------------------------------------------
 template <class E, int D>
@@ -1316,7 +1317,8 @@ __global__ void __launch_bounds__(256) build_kernel(BuildParams p) {
     const int idx = threadIdx.x + 256 * j;
     const int row = idx / kCols, col = idx % kCols;
     const int ti = min(ti0 + row, sg.ntok - 1);
-    const int64_t src = (int64_t(sg.src_row0 + ti) * p.Hkv + sg.h) * D + col * kVec;
+    const int tok = sg.pos_off < 0 ? ti : p.row_pos[sg.pos_off + ti];
+    const int64_t src = (int64_t(sg.src_row0 + tok) * p.Hkv + sg.h) * D + col * kVec;
     kr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kd + src));
     vr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vd + src));
     const int phys = p.v2p[sg.vstart + (ti >> lp)];

@@ -26,10 +26,11 @@ struct AttnParams {
 
 struct BuildSeg {
   int32_t chunk0;    // first 64-token copy unit of this segment in the launch
-  int32_t src_row0;  // dense row of the segment's first stored token
+  int32_t src_row0;  // dense row of the segment's first stored token (gather: of position 0)
   int32_t vstart;    // first virtual page of the segment
   int32_t ntok;
   int32_t h;
+  int32_t pos_off;  // -1: tokens are consecutive; else token i is at position row_pos[pos_off + i]
 };
 
 constexpr int kMaxBuildSegs = 128;
@@ -40,6 +41,7 @@ struct BuildParams {
   void* kp;
   void* vp;
   const int32_t* v2p;
+  const int32_t* row_pos;  // kept positions of RETRIEVAL segments (gather segments only)
   int32_t Hkv, P, nseg, nchunks;
   BuildSeg seg[kMaxBuildSegs];
 };

@@ -55,8 +55,11 @@ sp_status check_lengths_policy(int32_t B, const int32_t* ctx_len, const int32_t*
   if (pol == nullptr) return SP_ERR_INVALID_ARG;
   for (int32_t h = 0; h < Hkv; ++h) {
     if (pol[h].kind == SP_GLOBAL) continue;
-    if (pol[h].kind != SP_LOCAL && pol[h].kind != SP_LOCAL_ADAPTIVE) return SP_ERR_INVALID_ARG;
+    if (pol[h].kind != SP_LOCAL && pol[h].kind != SP_LOCAL_ADAPTIVE &&
+        pol[h].kind != SP_RETRIEVAL)
+      return SP_ERR_INVALID_ARG;
     if (pol[h].sink < 0 || pol[h].window < 1) return SP_ERR_INVALID_ARG;
+    if (pol[h].kind == SP_RETRIEVAL && pol[h].window > 1000) return SP_ERR_INVALID_ARG;
   }
   int64_t tot_ctx = 0, tot_q = 0;
   for (int32_t b = 0; b < B; ++b) {
@@ -76,6 +79,10 @@ sp_status check_shape(const Shape& s) {
     if (st != SP_OK) return st;
   }
   if (s.Hkv < 1 || s.Hq < 1 || s.Hq % s.Hkv != 0) return SP_ERR_INVALID_ARG;
+  if (s.mode == kModeDense && s.pol != nullptr) {  // its mask is positional only
+    for (int32_t h = 0; h < s.Hkv; ++h)
+      if (s.pol[h].kind == SP_RETRIEVAL) return SP_ERR_UNSUPPORTED;
+  }
   if (s.Hq / s.Hkv > kTileRows) return SP_ERR_UNSUPPORTED;
   st = check_lengths_policy(s.B, s.ctx_len, s.q_len, s.Hkv, s.pol);
   if (st != SP_OK) return st;
@@ -90,6 +97,14 @@ sp_head_policy effective_policy(const sp_head_policy& pol, int32_t L) {
   return sp_head_policy{SP_LOCAL, pol.sink, std::max<int32_t>(1, L / pol.window)};
 }
 
+void retrieval_counts(const sp_head_policy& pol, int32_t L, int32_t q, int32_t* n_sink,
+                      int32_t* n_kept) {
+  const int64_t prefix = std::max<int64_t>(0, int64_t(L) - q);
+  const int64_t s = std::min<int64_t>(pol.sink, prefix);
+  *n_sink = int32_t(s);
+  *n_kept = int32_t(ceil_div(int64_t(pol.window) * (prefix - s), 1000));
+}
+
 int head_segments(const sp_head_policy& pol_in, int32_t L, int32_t q, int32_t out_pos[2],
                   int32_t out_ntok[2]) {
   const sp_head_policy pol = effective_policy(pol_in, L);
@@ -98,6 +113,21 @@ int head_segments(const sp_head_policy& pol_in, int32_t L, int32_t q, int32_t ou
     out_pos[0] = 0;
     out_ntok[0] = L;
     return 1;
+  }
+  if (pol.kind == SP_RETRIEVAL) {
+    // The kept prefix tokens, compacted (positions come from the build's keep list), then
+    // the query chunk.
+    int32_t s = 0, k = 0, n = 0;
+    retrieval_counts(pol, L, q, &s, &k);
+    if (s + k > 0) {
+      out_pos[n] = 0;
+      out_ntok[n++] = s + k;
+    }
+    if (q > 0) {
+      out_pos[n] = L - q;
+      out_ntok[n++] = q;
+    }
+    return n;
   }
   const int64_t s = std::min<int64_t>(pol.sink, L);
   const int64_t r0 = std::max<int64_t>(0, int64_t(L) - q - pol.window + 1);
@@ -122,7 +152,8 @@ sp_status check_growable(int32_t B, const int32_t* ctx_len, const int32_t* reser
                          const sp_head_policy* pol) {
   if (B > 0 && reserve == nullptr) return SP_ERR_INVALID_ARG;
   for (int32_t h = 0; h < Hkv; ++h)
-    if (pol[h].kind == SP_LOCAL_ADAPTIVE) return SP_ERR_UNSUPPORTED;
+    if (pol[h].kind == SP_LOCAL_ADAPTIVE || pol[h].kind == SP_RETRIEVAL)
+      return SP_ERR_UNSUPPORTED;
   for (int32_t b = 0; b < B; ++b) {
     if (reserve[b] < 0 || (reserve[b] > 0 && ctx_len[b] < 1)) return SP_ERR_INVALID_ARG;
     if (int64_t(ctx_len[b]) + reserve[b] > kInt32Max) return SP_ERR_UNSUPPORTED;
@@ -259,6 +290,18 @@ void tile_ranges(const Shape& s, const HeadLayout* hl, const sp_head_policy& pol
   *rb = Range{0, 0, 0};
   if (s.mode == kModeDense || pol.kind == SP_GLOBAL) {
     *ra = Range{0, 0, pmax + 1};
+    return;
+  }
+  if (pol.kind == SP_RETRIEVAL) {
+    // Every kept prefix token is visible to every query of the chunk; the chunk (the last
+    // segment, starting at position L - q) is read up to the block's last query.
+    const Segment& chunk = hl->seg[hl->nseg - 1];
+    if (hl->nseg == 2) {
+      *ra = Range{0, 0, hl->seg[0].ntok};
+      *rb = Range{1, 0, pmax + 1 - chunk.pos};
+    } else {
+      *ra = Range{0, 0, pmax + 1 - chunk.pos};
+    }
     return;
   }
   const int32_t sink = std::min(pol.sink, L);
@@ -444,7 +487,8 @@ sp_status make_plan(const Shape& s, int32_t slots_prefill, int32_t slots_decode,
     for (int32_t h = 0; h < s.Hkv; ++h) {
       const sp_head_policy e = effective_policy(s.pol[h], s.ctx_len[b]);
       int32_t* d = &out->policy[(size_t(b) * s.Hkv + h) * 3];
-      d[0] = e.kind;
+      // A RETRIEVAL head stores only tokens its queries may see, bar the chunk's causal edge.
+      d[0] = e.kind == SP_RETRIEVAL ? int32_t(SP_GLOBAL) : e.kind;
       d[1] = e.kind == SP_LOCAL ? e.sink : 0;
       d[2] = e.kind == SP_LOCAL ? e.window : 1;
     }

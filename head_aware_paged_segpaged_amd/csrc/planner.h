@@ -49,6 +49,9 @@ sp_status check_shape(const Shape& s);
 // Policy of one head for a request of context length L: an SP_LOCAL_ADAPTIVE head becomes a
 // LOCAL head with window max(1, L / divisor); other heads are returned unchanged.
 sp_head_policy effective_policy(const sp_head_policy& pol, int32_t L);
+// Tokens a RETRIEVAL head keeps of its prefix: its sink, and the top fraction of the rest.
+void retrieval_counts(const sp_head_policy& pol, int32_t L, int32_t q, int32_t* n_sink,
+                      int32_t* n_kept);
 // Segments of one (request, KV head) following the layout rules of include/segpaged.h.
 int head_segments(const sp_head_policy& pol, int32_t L, int32_t q, int32_t out_pos[2],
                   int32_t out_ntok[2]);

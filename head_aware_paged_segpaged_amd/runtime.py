@@ -35,10 +35,13 @@ class SegPagedLayer:
         self.seg_table = self.kv_len = self.v2p = None
         self.workspace = None
         self.n_phys = 0
+        self.row_pos = None
+        self.importance = None
 
     def build(self, k_dense: torch.Tensor, v_dense: torch.Tensor, free_pages,
-              n_phys: int | None = None, stream=None) -> None:
-        """Allocate the pool and tables and fill them from dense [T, Hkv, D] K/V."""
+              n_phys: int | None = None, stream=None, importance=None) -> None:
+        """Allocate the pool and tables and fill them from dense [T, Hkv, D] K/V. Layouts with
+        RETRIEVAL heads need ``importance`` (host float32 [T, Hkv])."""
         fl = np.asarray(free_pages, dtype=np.int32)
         self.n_phys = int(n_phys if n_phys is not None else max(self.n_virt, 1))
         t = _TORCH[self.dtype]
@@ -53,12 +56,22 @@ class SegPagedLayer:
         self.seg_table = tables[:n_tab].view(Bn, self.Hkv, 2, 4)
         self.kv_len = tables[n_tab:n_tab + n_kl].view(Bn, self.Hkv)
         self.v2p = tables[n_tab + n_kl:]
+        if importance is not None:
+            self.importance = np.ascontiguousarray(np.asarray(importance, dtype=np.float32))
+            n_rows = B.segpaged_retrieval_rows(self.ctx_len, self.q_len, self.policy)
+            self.row_pos = torch.zeros((max(n_rows, 1),), dtype=torch.int32, device=self.device)
         self.rebuild(k_dense, v_dense, fl, stream)
 
     def rebuild(self, k_dense: torch.Tensor, v_dense: torch.Tensor, free_pages,
                 stream=None) -> None:
         """Refill the already allocated pool and tables (no allocation)."""
         fl = np.asarray(free_pages, dtype=np.int32)
+        if self.importance is not None:
+            B.segpaged_build_scored(self.dtype, self.D, self.P, self.ctx_len, self.q_len,
+                                    self.policy, self.importance, k_dense, v_dense, fl,
+                                    self.n_phys, self.k_pool, self.v_pool, self.seg_table,
+                                    self.kv_len, self.v2p, self.row_pos, stream)
+            return
         B.segpaged_build(self.dtype, self.D, self.P, self.ctx_len, self.q_len, self.policy,
                          k_dense, v_dense, fl, self.n_phys, self.k_pool, self.v_pool,
                          self.seg_table, self.kv_len, self.v2p, stream)

@@ -56,6 +56,16 @@
  *   any query of the chunk can see. Its segments, in position order, are
  *     (0, L) when R0 <= min(S, L);  (R0, L - R0) when S == 0;  else (0, S) and (R0, L - R0).
  *   A GLOBAL head has the single segment (0, L). L == 0 stores nothing.
+ * - A RETRIEVAL head (sink S, window = p in thousandths) keeps, of its prefix [0, L - q): the
+ *   first min(S, L - q) tokens and, of the n others, the ceil(p * n / 1000) with the highest
+ *   importance (an input: one float per (token, KV head); ties go to the lower position); and
+ *   the whole query chunk [L - q, L). Segments: the kept prefix tokens compacted in position
+ *   order (slot i holds the i-th kept position; its pos_start reads 0; the positions are
+ *   written to row_pos by segpaged_build_scored), then the chunk (L - q, q); with an empty
+ *   prefix the chunk alone. The tables depend only on (L, q, S, p); which tokens fill the first
+ *   segment depends on the importance. Every stored token is visible to every query of the
+ *   chunk up to the causal edge, so attention reads exactly its stored tokens. Not supported
+ *   by the dense-plus-mask path, growable layouts or several layers per build.
  * - seg_table int32 [B][Hkv][2][4] = {pos_start, n_tok, vpage_start, n_pages} per segment
  *   slot; an unused slot is {0, 0, running page total, 0}.
  * - Each segment starts on a fresh page; slot i of the segment's k-th page holds position
@@ -91,13 +101,22 @@ typedef enum sp_status {
 
 typedef enum sp_dtype { SP_BF16 = 0, SP_F32 = 1 } sp_dtype;
 
-typedef enum sp_head_kind { SP_GLOBAL = 0, SP_LOCAL = 1, SP_LOCAL_ADAPTIVE = 2 } sp_head_kind;
+typedef enum sp_head_kind {
+  SP_GLOBAL = 0,
+  SP_LOCAL = 1,
+  SP_LOCAL_ADAPTIVE = 2,
+  SP_RETRIEVAL = 3
+} sp_head_kind;
 
 /* One per KV head (page "RedKnot head classification": head types, defaults window 512 and
  * sink 4). `sink` and `window` are ignored for SP_GLOBAL heads. SP_LOCAL_ADAPTIVE follows the
  * same page's passage on windows that adapt to each request's context length (its example:
  * half the context): the head is LOCAL with window max(1, ctx_len[b] / window) for request b,
- * so `window` is a divisor >= 1. Any other kind is SP_ERR_INVALID_ARG. */
+ * so `window` is a divisor >= 1. SP_RETRIEVAL follows the same page's retrieval heads (full KV
+ * of which only the top-p important tokens are kept) and the closing summary of page "RedKnot
+ * SegPagedAttention runtime design" (retrieval heads take pages on demand): `window` is the
+ * kept fraction p in thousandths (1..1000); see the layout rules. Any other kind is
+ * SP_ERR_INVALID_ARG. */
 typedef struct sp_head_policy {
   int32_t kind;   /* sp_head_kind                         */
   int32_t sink;   /* S >= 0                               */
@@ -200,8 +219,34 @@ sp_status segpaged_build_layers(sp_dtype dtype, int32_t n_layers, int32_t B, int
  *                     entries rotate left by k (the dropped physical pages move to its end,
  *                     where later tokens reuse them); then the token goes to its end.
  * A ring thus keeps at most W + P - 1 tokens; fewer than P of them (all older than the window)
- * are stale, and attention masks them by position. Context-adaptive heads are not growable.
+ * are stale, and attention masks them by position. Context-adaptive and retrieval heads are
+ * not growable (SP_ERR_UNSUPPORTED).
  * --------------------------------------------------------------------------------------- */
+
+/* Number of kept-prefix rows of all SP_RETRIEVAL heads (the size of row_pos), in
+ * (request, head) order. Host only. */
+sp_status segpaged_retrieval_rows(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                                  int32_t Hkv, const sp_head_policy* pol, int64_t* n_rows);
+
+/* segpaged_build for layouts with SP_RETRIEVAL heads (page "RedKnot head classification":
+ * retrieval heads keep only the top-p important tokens; the selection happens once, at
+ * KV-write time, like the rest of the layout). Same arguments and errors as segpaged_build,
+ * plus:
+ *   importance : host float [sum(ctx_len)][Hkv], token-major like k_dense; only the prefix
+ *                tokens of RETRIEVAL heads are read; a non-finite value there is
+ *                SP_ERR_INVALID_ARG.
+ *   row_pos    : device int32 [segpaged_retrieval_rows] (written): the kept positions of each
+ *                RETRIEVAL head, ascending, heads in (request, head) order; may be NULL when
+ *                that count is 0.
+ * segpaged_build (and the _layers build) returns SP_ERR_INVALID_ARG for layouts that keep
+ * RETRIEVAL rows, since it has no importance. */
+sp_status segpaged_build_scored(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D,
+                                int32_t page_size, const int32_t* ctx_len, const int32_t* q_len,
+                                const sp_head_policy* pol, const float* importance,
+                                const void* k_dense, const void* v_dense,
+                                const int32_t* free_pages, int64_t n_free, int64_t n_phys,
+                                void* k_pool, void* v_pool, int32_t* seg_table, int32_t* kv_len,
+                                int32_t* v2p, int32_t* row_pos, hipStream_t stream);
 
 /* Pages (n_virt) and host tables of the growable layout. reserve: host int32 [B] >= 0; a
  * request with reserve[b] > 0 needs ctx_len[b] >= 1. Errors as segpaged_plan_pages /

@@ -83,7 +83,9 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert _err(sp.segpaged_plan_pages, [10], [1], [(7, 2, 3)], 16) == E.SP_ERR_INVALID_ARG
     assert _err(sp.segpaged_plan_pages, [10], [1], [(2, 2, 0)], 16) == E.SP_ERR_INVALID_ARG
     assert _err(sp.segpaged_plan_pages, [10], [1], [(2, -1, 2)], 16) == E.SP_ERR_INVALID_ARG
-    assert _err(sp.segpaged_plan_pages, [10], [1], [(3, 2, 2)], 16) == E.SP_ERR_INVALID_ARG
+    assert _err(sp.segpaged_plan_pages, [10], [1], [(4, 2, 2)], 16) == E.SP_ERR_INVALID_ARG
+    assert _err(sp.segpaged_plan_pages, [10], [1], [(3, 2, 1001)], 16) == E.SP_ERR_INVALID_ARG
+    assert _err(sp.segpaged_plan_pages, [10], [1], [(3, 2, 0)], 16) == E.SP_ERR_INVALID_ARG
     assert _err(sp.segpaged_plan_pages, [10], [1], pol, 48) == E.SP_ERR_UNSUPPORTED
     assert _err(sp.segpaged_plan_pages, [10], [1], pol, 8) == E.SP_ERR_UNSUPPORTED
     # attention shape checks run before any device query
@@ -221,3 +223,43 @@ def test_growable_and_append_invalid_arguments():
     bad = list(args(pol, 1))
     bad[15] = 0  # n_virt
     assert lib.segpaged_append(*bad) == binding.SP_ERR_INVALID_ARG
+
+
+def test_retrieval_layout_tables_and_invalid_arguments():
+    rng = np.random.default_rng(41)
+    for _ in range(200):
+        B, Hkv = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        P = int(rng.choice([16, 64, 256]))
+        ctx = rng.integers(0, 900, size=B)
+        q = np.array([rng.integers(0, c + 1) for c in ctx])
+        pol = [(3, int(rng.integers(0, 9)), int(rng.integers(1, 1001))) if rng.random() < 0.6
+               else (int(rng.integers(0, 2)), int(rng.integers(0, 9)), int(rng.integers(1, 300)))
+               for _ in range(Hkv)]
+        seg, kvl = sp.segpaged_layout_tables(ctx, q, pol, P)
+        seg_o, kvl_o, n_virt = plan_tables(ctx, q, pol, P)
+        np.testing.assert_array_equal(seg, seg_o)
+        np.testing.assert_array_equal(kvl, kvl_o)
+        rows = sum(seg_o[b, h, 0, 1] for b in range(B) for h in range(Hkv)
+                   if pol[h][0] == 3 and ctx[b] - q[b] > 0)
+        assert sp.segpaged_retrieval_rows(ctx, q, pol) == rows
+    E = binding
+    pol = [(3, 4, 100)]
+    with pytest.raises(sp.SegPagedError) as e:  # the dense-plus-mask path cannot mask it
+        sp.segpaged_dense_mask_workspace_size("bf16", 1, 1, 128, [100], [1], pol)
+    assert e.value.status == E.SP_ERR_UNSUPPORTED
+    with pytest.raises(sp.SegPagedError) as e:
+        sp.segpaged_plan_pages_growable([100], [1], [4], pol, 64)
+    assert e.value.status == E.SP_ERR_UNSUPPORTED
+    lib = binding.lib()
+    fake = binding._vp(256)
+    c, ql, p = (np.array(x, np.int32) for x in ([100], [1], pol))
+    # the plain build has no importance for the kept rows; the scored build rejects NaN
+    assert lib.segpaged_build(0, 1, 1, 128, 64, binding._ptr(c), binding._ptr(ql),
+                              binding._ptr(p), fake, fake, binding._ptr(np.arange(4, dtype=np.int32)),
+                              4, 4, fake, fake, fake, fake, fake, None) == E.SP_ERR_INVALID_ARG
+    imp = np.ones((100, 1), np.float32)
+    imp[50, 0] = np.nan
+    assert lib.segpaged_build_scored(0, 1, 1, 128, 64, binding._ptr(c), binding._ptr(ql),
+                                     binding._ptr(p), binding._ptr(imp), fake, fake,
+                                     binding._ptr(np.arange(4, dtype=np.int32)), 4, 4, fake,
+                                     fake, fake, fake, fake, fake, None) == E.SP_ERR_INVALID_ARG

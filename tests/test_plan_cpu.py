@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from head_aware_paged_segpaged_amd import segpaged_attention_plan_host
-from workloads import GLOBAL, LOCAL, LOCAL_ADAPTIVE, config_case, custom_case
+from workloads import GLOBAL, LOCAL, LOCAL_ADAPTIVE, RETRIEVAL, config_case, custom_case
 
 STEP = 64          # stored slots per KV step
 TILE_ROWS = 128    # rows of a prefill item
@@ -54,6 +54,15 @@ def visible_slots(case, b, h, t0, nq):
     segs = oracle.segments(kind, sink, window, L, q)
     p = np.arange(L - q + t0, L - q + t0 + nq)
     out = set()
+    if kind == RETRIEVAL:
+        # the kept prefix tokens (the first segment unless the prefix is empty) are all
+        # visible; the chunk is read causally
+        for s, (pos0, n) in enumerate(segs):
+            if pos0 == L - q and s == len(segs) - 1 and q > 0:
+                out.update((s, i) for i in range(int(p.max()) + 1 - pos0))
+            else:
+                out.update((s, i) for i in range(n))
+        return out
     for s, (pos0, n) in enumerate(segs):
         j = np.arange(pos0, pos0 + n)
         seen = oracle.visible(kind, sink, window, p[:, None], j[None, :]).any(axis=0)
@@ -129,6 +138,8 @@ def test_plan_random_shapes():
             r = rng.random()
             if r < 0.3:
                 pol.append((GLOBAL, 0, 1))
+            elif r < 0.42:  # top fraction of the prefix by importance, sink, chunk
+                pol.append((RETRIEVAL, int(rng.choice([0, 4])), int(rng.choice([1, 100, 999, 1000]))))
             elif r < 0.5:  # window = context length // divisor, per request
                 pol.append((LOCAL_ADAPTIVE, int(rng.choice([0, 4])), int(rng.choice([1, 2, 5, 40]))))
             else:

@@ -72,7 +72,7 @@ class Case:
         return int(self.q_len.sum())
 
 
-# The five workloads. "draw_L" / "draw_global" say how the meta stream is used.
+# The workloads. "draw_L" / "draw_global" say how the meta stream is used.
 CONFIGS = [
     dict(name="tiny_fp32_L512", dtype="f32", Hq=8, Hkv=4, D=64, P=16, B=1,
          L=("fixed", [512]), q=("fixed", 64), globals=("fixed", [0]),
@@ -98,6 +98,13 @@ CONFIGS = [
     dict(name="qwen3_32b_decode_b64_4k_128k_half_window", dtype="bf16", Hq=64, Hkv=8, D=128,
          P=64, B=64, L=("log_uniform", 4096, 131072), q=("fixed", 1), globals=("draw", 2),
          sink=4, window=2, local_kind=LOCAL_ADAPTIVE, q_std=1.0 / math.sqrt(128), kv_std=1.0),
+    # The decode workload (same seed: same lengths, GLOBAL heads and tensors) with its first
+    # two LOCAL heads turned into RETRIEVAL heads that keep sink 4 and the top 10 % of their
+    # prefix by importance (``importance_scores``).
+    dict(name="qwen3_32b_decode_b64_4k_128k_retrieval", dtype="bf16", Hq=64, Hkv=8, D=128,
+         P=64, B=64, L=("log_uniform", 4096, 131072), q=("fixed", 1), globals=("draw", 2),
+         sink=4, window=512, retrieval=(2, 100), seed=4, q_std=1.0 / math.sqrt(128),
+         kv_std=1.0),
 ]
 
 
@@ -164,7 +171,7 @@ def _policy_table(Hkv: int, global_heads, sink: int, window: int,
 def config_case(index: int, seed: int | None = None, with_tensors: bool = True) -> Case:
     """Workload ``index`` (0-based into ``CONFIGS``); the seed defaults to ``index + 1``."""
     cfg = CONFIGS[index]
-    seed = index + 1 if seed is None else seed
+    seed = cfg.get("seed", index + 1) if seed is None else seed
     rng = _meta_rng(seed)
     B = cfg["B"]
     kind = cfg["L"][0]
@@ -185,6 +192,10 @@ def config_case(index: int, seed: int | None = None, with_tensors: bool = True) 
     else:
         ghs = sorted(int(h) for h in rng.choice(cfg["Hkv"], gv, replace=False))
     pol = _policy_table(cfg["Hkv"], ghs, cfg["sink"], cfg["window"], cfg.get("local_kind", LOCAL))
+    if "retrieval" in cfg:
+        n_r, permille = cfg["retrieval"]
+        for h in [h for h in range(cfg["Hkv"]) if pol[h, 0] != GLOBAL][:n_r]:
+            pol[h] = (RETRIEVAL, cfg["sink"], permille)
     case = Case(name=cfg["name"], dtype=cfg["dtype"], B=B, Hq=cfg["Hq"], Hkv=cfg["Hkv"],
                 D=cfg["D"], P=cfg["P"], ctx_len=ctx, q_len=q, policy=pol,
                 scale=1.0 / math.sqrt(cfg["D"]), seed=seed)
