@@ -180,6 +180,12 @@ def main() -> int:
                     help="decode workloads: also time N decode steps over a growable layout, "
                          "each appending every request's new token (segpaged_append) and then "
                          "attending (segpaged_decode); reported as decode_append; 0 skips it")
+    ap.add_argument("--decode-graph", action="store_true",
+                    help="with --decode-steps: also time the steps as replays of one captured "
+                         "HIP graph (append + decode), inputs copied into its buffers per step")
+    ap.add_argument("--decode-requests", type=int, default=0, metavar="R",
+                    help="with --decode-steps: only the workload's first R requests (a small "
+                         "decode batch, where launch costs matter); 0 = all")
     ap.add_argument("--gemm-reference", action="store_true",
                     help="only time torch's bf16 GEMM (hipBLASLt) at 4096^3..16384^3: what a "
                          "vendor-tuned dense contraction reaches on this GPU, for context")
@@ -429,27 +435,31 @@ def decode_append_leg(args, case, k, v, up, evict, stream, planned_ms, decoder_c
         return {"skipped": "needs a decode workload (one query per request) without "
                            "context-adaptive or retrieval heads"}
     n_steps, n_warm = args.decode_steps, args.warmup
-    total = n_steps + n_warm
+    total = n_steps + 2 * n_warm
+    R = case.B if args.decode_requests <= 0 else min(args.decode_requests, case.B)
     kn, vn, qn = decode_tokens(case, total)
-    kn, vn, qn = up(kn), up(vn), up(qn)
-    reserve = np.full(case.B, total, dtype=np.int32)
-    dec = decoder_cls(case.dtype, case.Hq, case.Hkv, case.D, case.P, case.ctx_len, case.q_len,
-                      reserve, case.policy, k.device)
+    kn, vn, qn = (up(np.ascontiguousarray(x[:, :R])) for x in (kn, vn, qn))
+    ctx, ql = case.ctx_len[:R], case.q_len[:R]
+    rows = int(ctx.sum())
+    k, v = k[:rows].contiguous(), v[:rows].contiguous()
+    reserve = np.full(R, total + n_steps, dtype=np.int32)
+    dec = decoder_cls(case.dtype, case.Hq, case.Hkv, case.D, case.P, ctx, ql, reserve,
+                      case.policy, k.device)
     dec.build(k, v, free_list(case.seed, dec.n_virt))
     dec.plan()
     out = torch.empty_like(qn[0])
     local = case.policy[:, 0] != 0
 
-    def rows():
+    def rows_of():
         kl = dec.kv_len.cpu().numpy().astype(np.int64)
         return int(kl[:, local].sum()), int(kl[:, ~local].sum())
 
-    rows0 = rows()
+    rows0 = rows_of()
     for i in range(n_warm):
         dec.append(kn[i], vn[i])
         dec.decode(qn[i], case.scale, out=out)
     torch.cuda.synchronize()
-    rows_w = rows()
+    rows_w = rows_of()
     ev_a = {i: (event_cls(), event_cls()) for i in range(0, n_steps, EVENT_EVERY)}
     evict()
     e0, e1 = event_cls(), event_cls()
@@ -469,19 +479,44 @@ def decode_append_leg(args, case, k, v, up, evict, stream, planned_ms, decoder_c
     append_ms = float(np.mean([a.elapsed_ms(b) for a, b in ev_a.values()]))
     err = dec.check()
     assert err == (0, 0), "device-side error %r" % (err,)
-    rows1 = rows()
+    rows1 = rows_of()
+    graph = None
+    if args.decode_graph:
+        # the same kind of step as replays of one captured graph: the next token's rows and
+        # queries are copied into the graph's buffers (on the stream) before each replay
+        bufs = [kn[0].clone(), vn[0].clone(), qn[0].clone()]
+        g = dec.capture_step(bufs[0], bufs[1], bufs[2], out, case.scale)
+        base = n_warm + n_steps
+        for i in range(n_warm):
+            for buf, src in zip(bufs, (kn, vn, qn)):
+                buf.copy_(src[base + i])
+            g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = event_cls(), event_cls()
+        g0.record(stream)
+        for i in range(n_steps):
+            for buf, src in zip(bufs, (kn, vn, qn)):
+                buf.copy_(src[(base + n_warm + i) % total])
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        dec.advance(n_warm + n_steps)
+        gms = g0.elapsed_ms(g1) / n_steps
+        err = dec.check()
+        assert err == (0, 0), "device-side error %r" % (err,)
+        graph = {"ms_per_step": round(gms, 5), "vs_eager": round(gms / ms, 3)}
     elem = 2 if case.dtype == "bf16" else 4
     # mean stored rows read per step (GLOBAL heads grow by one row a step)
     read_rows = (sum(rows_w) + sum(rows1)) / 2.0
-    step_bytes = (2.0 * read_rows * case.D * elem + 2.0 * case.B * case.Hq * case.D * elem
-                  + 2.0 * 2.0 * case.B * case.Hkv * case.D * elem)  # + the appended rows
+    step_bytes = (2.0 * read_rows * case.D * elem + 2.0 * R * case.Hq * case.D * elem
+                  + 2.0 * 2.0 * R * case.Hkv * case.D * elem)  # + the appended rows
     gbps = step_bytes / ((ms - append_ms) * 1e-3) / 1e9
-    return {"steps": n_steps, "warmup": n_warm, "ms_per_step": round(ms, 5),
-            "append_ms": round(append_ms, 5), "tokens_per_s": round(case.B / (ms * 1e-3), 1),
+    return {"requests": R, "steps": n_steps, "warmup": n_warm, "ms_per_step": round(ms, 5),
+            "append_ms": round(append_ms, 5), "tokens_per_s": round(R / (ms * 1e-3), 1),
             "decode_gbps": round(gbps, 1), "decode_hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
-            "vs_planned_step": round(ms / planned_ms, 3),
+            "vs_planned_step": round(ms / planned_ms, 3) if R == case.B else None,
             "local_rows": [rows0[0], rows1[0]], "global_rows": [rows0[1], rows1[1]],
-            "pages_owned": int(dec.n_virt)}
+            "pages_owned": int(dec.n_virt), "graph": graph}
 
 
 def build_layers_leg(n_layers, case, k, v, evict, stream, layers_cls, event_cls,

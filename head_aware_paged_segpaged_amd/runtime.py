@@ -259,6 +259,31 @@ class SegPagedDecoder:
                           self.v2p, scale, out, self.workspace, stream)
         return out
 
+    def capture_step(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                     out: torch.Tensor, scale: float) -> torch.cuda.CUDAGraph:
+        """Captures one decode step (append every request's token from k_new / v_new, then
+        decode q into out) as a HIP graph. The step launches only kernels: no host work, no
+        copies, no memsets, no synchronisation. Replay it after writing the next token's rows
+        and queries into the same buffers; each replay appends one token per request, so the
+        reserve bounds the number of replays. ``ctx_now`` is not advanced by replays; call
+        ``advance(n)`` to keep it for re-planning."""
+        if self.workspace is None:
+            self.plan()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            B.segpaged_append(self.dtype, self.D, self.P, self.policy, None, k_new, v_new,
+                              self.k_pool, self.v_pool, self.n_phys, self.seg_table,
+                              self.kv_len, self.v2p, self.error)
+            B.segpaged_decode(self.dtype, self.Hq, self.Hkv, self.D, self.P, self.policy, q,
+                              self.k_pool, self.v_pool, self.n_phys, self.seg_table, self.kv_len,
+                              self.v2p, scale, out, self.workspace)
+        return graph
+
+    def advance(self, n: int = 1) -> None:
+        """Records n appends of every request made outside ``append`` (graph replays)."""
+        self.ctx_now = self.ctx_now + int(n)
+
     def check(self, stream=None) -> tuple[int, int]:
         """(append error word, decode workspace error word); reading clears both."""
         torch.cuda.synchronize()

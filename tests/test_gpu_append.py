@@ -244,3 +244,40 @@ def test_full_size_decode_append_sampled(index):
     print("%s append sampled: maxabs=%.3e min_cos=%.8f" % (c.name, worst_abs, worst_cos),
           flush=True)
     assert worst_abs <= MAXABS[c.dtype] and worst_cos > COS_MIN
+
+
+def test_decode_step_graph_replays_match_eager():
+    # One decode step (append + table-driven decode) captured as a HIP graph and replayed with
+    # new inputs copied into its buffers between replays, against the same steps run eagerly
+    # on an identical layout: every replay's output and tables bitwise equal.
+    from workloads import decode_tokens
+    pol = [(GLOBAL, 0, 1), (LOCAL, 0, 40), (LOCAL, 4, 100), (GLOBAL, 0, 1)]
+    ctx, steps = np.array([300, 1200, 77]), 30
+    c = custom_case(780, dtype="bf16", Hq=16, Hkv=4, D=128, P=16, ctx_len=ctx, q_len=[1, 1, 1],
+                    policy=pol)
+    print("case graph replay", flush=True)
+    kn, vn, qn = decode_tokens(c, steps)
+    kd, vd, qd = to_device(kn, "bf16"), to_device(vn, "bf16"), to_device(qn, "bf16")
+    decs = []
+    for _ in range(2):
+        d = SegPagedDecoder("bf16", 16, 4, 128, 16, ctx, c.q_len, np.full(3, steps), pol, DEV)
+        d.build(to_device(c.k, "bf16"), to_device(c.v, "bf16"), free_list(780, d.n_virt))
+        d.plan()
+        decs.append(d)
+    eager, graphed = decs
+    k_buf, v_buf, q_buf = kd[0].clone(), vd[0].clone(), qd[0].clone()
+    out_buf = torch.empty_like(q_buf)
+    g = graphed.capture_step(k_buf, v_buf, q_buf, out_buf, c.scale)
+    for t in range(steps):
+        k_buf.copy_(kd[t])
+        v_buf.copy_(vd[t])
+        q_buf.copy_(qd[t])
+        g.replay()
+        graphed.advance()
+        eager.append(kd[t], vd[t])
+        oe = eager.decode(qd[t], c.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out_buf, oe), t
+        assert torch.equal(graphed.seg_table, eager.seg_table)
+        assert torch.equal(graphed.v2p, eager.v2p)
+    assert graphed.check() == (0, 0) and eager.check() == (0, 0)

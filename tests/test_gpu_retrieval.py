@@ -151,3 +151,15 @@ def test_full_size_retrieval_workload_sampled():
         worst_cos = min(worst_cos, float(g @ ref / (np.linalg.norm(g) * np.linalg.norm(ref))))
     print("%s sampled: maxabs=%.3e min_cos=%.8f" % (c.name, worst_abs, worst_cos), flush=True)
     assert worst_abs <= MAXABS[c.dtype] and worst_cos > COS_MIN
+
+
+@pytest.mark.parametrize("dtype,P", [("bf16", 256), ("f32", 16)])
+def test_retrieval_edge_requests(dtype, P):
+    # one request with no queries (its kept prefix is stored, nothing attends), one whose whole
+    # context is the query chunk (no prefix: the chunk alone), one decode request, and sinks
+    # longer than the prefix
+    pol = [(RETRIEVAL, 4, 1), (RETRIEVAL, 700, 500), (GLOBAL, 0, 1), (RETRIEVAL, 0, 1000)]
+    c = custom_case(960 + P, dtype=dtype, Hq=8, Hkv=4, D=128 if dtype == "bf16" else 64, P=P,
+                    ctx_len=[500, 90, 1300, 7], q_len=[0, 90, 1, 3], policy=pol)
+    print("case retrieval edges", dtype, P, flush=True)
+    _run(c, importance_scores(c, levels=2))
