@@ -39,13 +39,16 @@ The pages give no decode-time algorithm; the readings taken here:
    ceil(S / P) + ceil(min(Lmax - S_pg, W + P - 1) / P) (after it); a sink segment its pages.
    Appending into a full segment is an error.
 6. Context-adaptive LOCAL windows change W as the context grows; they are not growable here.
+7. A RETRIEVAL head grows like a GLOBAL one: appended tokens join its last segment, the query
+   chunk, which owns ceil((q + reserve) / P) pages; its kept prefix segment never changes. A
+   growable request needs a non-empty chunk (q >= 1) for its retrieval heads.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from .plan import GLOBAL, LOCAL, segments
+from .plan import GLOBAL, LOCAL, RETRIEVAL, segments
 
 
 def _cdiv(a: int, b: int) -> int:
@@ -60,6 +63,10 @@ def owned_pages(kind: int, sink: int, window: int, L: int, q: int, reserve: int,
     lmax = L + reserve
     if kind == GLOBAL:
         return segs, [_cdiv(lmax, P)]
+    if kind == RETRIEVAL:  # the chunk (the last segment) grows; the kept prefix does not
+        own = [_cdiv(n, P) for _, n in segs]
+        own[-1] = _cdiv(segs[-1][1] + reserve, P)
+        return segs, own
     if sink > 0 and len(segs) == 1:  # sink and window in one segment (0, L)
         s_pg = _cdiv(sink, P) * P
         own = max(_cdiv(L, P), _cdiv(min(lmax, s_pg + window - 1), P))
@@ -84,8 +91,10 @@ def grow_tables(ctx_len, q_len, reserve, policy, P: int):
             raise ValueError("a request that grows needs a non-empty context")
         for h in range(Hkv):
             kind, sink, window = (int(x) for x in policy[h])
-            if kind not in (GLOBAL, LOCAL):
-                raise ValueError("growable layouts take GLOBAL and LOCAL heads")
+            if kind not in (GLOBAL, LOCAL, RETRIEVAL):
+                raise ValueError("growable layouts take GLOBAL, LOCAL and RETRIEVAL heads")
+            if kind == RETRIEVAL and R > 0 and q < 1:
+                raise ValueError("a growing retrieval head needs a non-empty query chunk")
             segs, own = owned_pages(kind, sink, window, L, q, R, P)
             for s in range(2):
                 if s < len(segs):
@@ -121,6 +130,8 @@ def append_step(seg_table, kv_len, v2p, policy, P: int, n_new=None):
             L = max(ends)  # the newest stored token is the last one of the context
             r0 = max(0, L + 1 - window)  # window start of the query at position L
             target = 0
+            if kind == RETRIEVAL:
+                target = 1 if rows[1][3] > 0 else 0  # the query chunk
             if kind == LOCAL:
                 ring = 0 if sink == 0 else None
                 if sink > 0 and rows[1][3] > 0:

@@ -36,24 +36,27 @@ def test_worked_example():
         assert [list(w) for w in writes] == step["writes"]
 
 
-def _random_policy(rng, Hkv, P):
+def _random_policy(rng, Hkv, P, retrieval=False):
     pol = []
     for h in range(Hkv):
         if h == 0 or rng.random() < 0.25:
             pol.append((oracle.GLOBAL, 0, 1))
+        elif retrieval and rng.random() < 0.4:
+            pol.append((oracle.RETRIEVAL, int(rng.integers(0, P)), int(rng.integers(1, 1001))))
         else:
             pol.append((oracle.LOCAL, int(rng.integers(0, 2 * P)), int(rng.integers(1, 5 * P))))
     return pol
 
 
-def test_reserve_zero_is_the_build_layout():
-    rng = np.random.default_rng(11)
+@pytest.mark.parametrize("retrieval", [False, True])
+def test_reserve_zero_is_the_build_layout(retrieval):
+    rng = np.random.default_rng(11 + retrieval)
     for _ in range(200):
         P = int(rng.choice([4, 8, 16]))
         B, Hkv = int(rng.integers(1, 4)), int(rng.integers(1, 5))
         ctx = rng.integers(0, 12 * P, size=B)
         q = np.array([int(rng.integers(0, c + 1)) if c else 0 for c in ctx])
-        pol = _random_policy(rng, Hkv, P)
+        pol = _random_policy(rng, Hkv, P, retrieval)
         a = grow_tables(ctx, q, np.zeros(B, dtype=np.int64), pol, P)
         b = oracle.plan_tables(ctx, q, pol, P)
         np.testing.assert_array_equal(a[0], b[0])
@@ -61,8 +64,8 @@ def test_reserve_zero_is_the_build_layout():
         assert a[2] == b[2]
 
 
-def _stored(st, v2p, P, b, h):
-    return oracle.gather_positions(st, v2p, P, b, h)
+def _stored(st, v2p, P, b, h, kept=None):
+    return oracle.gather_positions(st, v2p, P, b, h, kept)
 
 
 def _head_pages(st, v2p, b, h):
@@ -74,28 +77,38 @@ def _head_pages(st, v2p, b, h):
     return sorted(out)
 
 
-def _trajectory(rng, P, B, Hkv, steps, pol=None, q_one=False):
+def _trajectory(rng, P, B, Hkv, steps, pol=None, q_one=False, retrieval=False):
     ctx = rng.integers(1, 10 * P, size=B)
     q = np.ones(B, dtype=np.int64) if q_one else np.array([int(rng.integers(1, c + 1)) for c in ctx])
     reserve = np.full(B, steps, dtype=np.int64)
-    pol = pol or _random_policy(rng, Hkv, P)
+    pol = pol or _random_policy(rng, Hkv, P, retrieval)
     st, kl, nv = grow_tables(ctx, q, reserve, pol, P)
     v2p = rng.permutation(nv + 5)[:nv].astype(np.int32)  # a free list with spare pages
     return ctx, q, pol, st, kl, v2p
 
 
-def test_append_trajectory_invariants():
-    rng = np.random.default_rng(12)
+@pytest.mark.parametrize("retrieval", [False, True])
+def test_append_trajectory_invariants(retrieval):
+    # With RETRIEVAL heads, a stand-in keep list (every other prefix token, as many as the
+    # head keeps) names the positions of the kept segment; growth never touches it.
+    rng = np.random.default_rng(12 + retrieval)
     for case in range(60):
         P = int(rng.choice([4, 8, 16]))
         B, Hkv = int(rng.integers(1, 3)), int(rng.integers(2, 5))
         steps = int(rng.integers(1, 8 * P))
-        ctx, q, pol, st, kl, v2p = _trajectory(rng, P, B, Hkv, steps)
+        ctx, q, pol, st, kl, v2p = _trajectory(rng, P, B, Hkv, steps, retrieval=retrieval)
+        kept = {}
+        for b in range(B):
+            for h in range(Hkv):
+                if pol[h][0] == oracle.RETRIEVAL and ctx[b] - q[b] > 0:
+                    s_, k_ = oracle.retrieval_counts(pol[h][1], pol[h][2], ctx[b], q[b])
+                    cand = list(range(s_, ctx[b] - q[b]))
+                    kept[(b, h)] = list(range(s_)) + sorted(cand[::2] + cand[1::2])[:k_]
         owned0 = {(b, h): _head_pages(st, v2p, b, h) for b in range(B) for h in range(Hkv)}
         pool = {}
         for b in range(B):
             for h in range(Hkv):
-                for pos, ph, sl in _stored(st, v2p, P, b, h):
+                for pos, ph, sl in _stored(st, v2p, P, b, h, kept.get((b, h))):
                     assert (ph, sl) not in pool
                     pool[(ph, sl)] = (b, h, pos)
         L = ctx.copy()
@@ -110,13 +123,14 @@ def test_append_trajectory_invariants():
             for b in range(B):
                 for h in range(Hkv):
                     kind, sink, window = pol[h]
-                    got = _stored(st, v2p, P, b, h)
+                    got = _stored(st, v2p, P, b, h, kept.get((b, h)))
                     pos = np.array(sorted(p for p, _, _ in got))
                     assert len(pos) == kl[b, h] and len(set(pos.tolist())) == len(pos)
                     for p_, ph, sl in got:  # every stored token still holds its own row
                         assert pool[(ph, sl)] == (b, h, p_)
                     p_q = L[b] - 1  # the next decode query
-                    vis = np.nonzero(visible(kind, sink, window, p_q, np.arange(L[b])))[0]
+                    vis = np.nonzero(visible(kind, sink, window, p_q, np.arange(L[b]),
+                                             kept.get((b, h), []), ctx[b] - q[b]))[0]
                     assert set(vis.tolist()) <= set(pos.tolist()), (case, t, b, h)
                     stale = sorted(set(pos.tolist()) - set(vis.tolist()))
                     if kind == oracle.GLOBAL:
@@ -181,6 +195,19 @@ def test_owned_pages_closed_forms():
     # split head after a 300-token prefill chunk: the ring keeps its build pages
     segs, own = owned_pages(oracle.LOCAL, 4, 64, 1000, 300, 500, P)
     assert segs == [(0, 4), (637, 363)] and own == [1, 23]
+
+
+def test_retrieval_growth_closed_form():
+    # L = 100, q = 10, S = 4, p = 250, reserve 30, P = 16: the kept prefix (26 tokens) keeps its
+    # 2 pages, the chunk owns ceil((10 + 30) / 16) = 3; each append lands in the chunk.
+    pol = [(oracle.RETRIEVAL, 4, 250)]
+    st, kl, nv = grow_tables([100], [10], [30], pol, 16)
+    assert st[0, 0].tolist() == [[0, 26, 0, 2], [90, 10, 2, 3]] and nv == 5
+    st2, kl2, v2p, w = append_step(st, kl, np.arange(nv), pol, 16)
+    assert st2[0, 0].tolist() == [[0, 26, 0, 2], [90, 11, 2, 3]] and kl2[0, 0] == 37
+    assert w == [(0, 0, 100, 2, 10)]
+    with pytest.raises(ValueError):  # a growing retrieval head needs a query chunk
+        grow_tables([100], [0], [30], pol, 16)
 
 
 def test_adaptive_and_empty_context_rejected():
