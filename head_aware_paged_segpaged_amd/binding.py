@@ -87,7 +87,7 @@ _SIGS = {
                               _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "segpaged_retrieval_rows": (_i32, [_i32, _vp, _vp, _i32, _vp, ctypes.POINTER(_i64)]),
     "segpaged_build_scored": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
-                                     _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+                                     _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "segpaged_plan_pages_growable": (_i32, [_i32, _vp, _vp, _vp, _i32, _vp, _i32,
                                             ctypes.POINTER(_i64)]),
     "segpaged_layout_tables_growable": (_i32, [_i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp]),
@@ -267,13 +267,16 @@ def segpaged_retrieval_rows(ctx_len, q_len, policy) -> int:
 
 def segpaged_build_scored(dtype, D: int, page_size: int, ctx_len, q_len, policy, importance,
                           k_dense, v_dense, free_pages, n_phys: int, k_pool, v_pool, seg_table,
-                          kv_len, v2p, row_pos, stream=None) -> None:
-    """importance: host float32 [sum(ctx_len)][Hkv]; row_pos: device int32 (or None)."""
+                          kv_len, v2p, row_pos, stream=None, reserve=None) -> None:
+    """importance: host float32 [sum(ctx_len)][Hkv]; row_pos: device int32 (or None);
+    reserve: host [B] (growable layout) or None."""
     c, q, p = _host_i32(ctx_len), _host_i32(q_len), _host_i32(policy).reshape(-1, 3)
     fl = _host_i32(free_pages)
+    r = _host_i32(reserve) if reserve is not None else None
     imp = np.ascontiguousarray(np.asarray(importance, dtype=np.float32))
     _check(lib().segpaged_build_scored(_dtype_code(dtype), len(c), p.shape[0], D, page_size,
-                                       _ptr(c), _ptr(q), _ptr(p), _ptr(imp),
+                                       _ptr(c), _ptr(q), _ptr(r) if r is not None else None,
+                                       _ptr(p), _ptr(imp),
                                        _dev(k_dense, "k_dense"), _dev(v_dense, "v_dense"),
                                        _ptr(fl), fl.size, n_phys, _dev(k_pool, "k_pool"),
                                        _dev(v_pool, "v_pool"), _dev(seg_table, "seg_table"),

@@ -170,7 +170,7 @@ sp_status layout_impl(int32_t n_layers, int32_t B, const int32_t* ctx_len, const
   if (st != SP_OK) return st;
   if (reserve != nullptr) {
     if (n_layers != 1) return SP_ERR_INVALID_ARG;
-    st = check_growable(B, ctx_len, reserve, Hkv, pol);
+    st = check_growable(B, ctx_len, q_len, reserve, Hkv, pol);
     if (st != SP_OK) return st;
   }
   return make_layout_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size, reserve, lay);
@@ -467,12 +467,13 @@ sp_status segpaged_retrieval_rows(int32_t B, const int32_t* ctx_len, const int32
 
 sp_status segpaged_build_scored(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D,
                                 int32_t page_size, const int32_t* ctx_len, const int32_t* q_len,
-                                const sp_head_policy* pol, const float* importance,
-                                const void* k_dense, const void* v_dense,
-                                const int32_t* free_pages, int64_t n_free, int64_t n_phys,
-                                void* k_pool, void* v_pool, int32_t* seg_table, int32_t* kv_len,
-                                int32_t* v2p, int32_t* row_pos, hipStream_t stream) {
-  return build_impl(dtype, 1, B, Hkv, D, page_size, ctx_len, q_len, nullptr, pol, k_dense,
+                                const int32_t* reserve, const sp_head_policy* pol,
+                                const float* importance, const void* k_dense,
+                                const void* v_dense, const int32_t* free_pages, int64_t n_free,
+                                int64_t n_phys, void* k_pool, void* v_pool, int32_t* seg_table,
+                                int32_t* kv_len, int32_t* v2p, int32_t* row_pos,
+                                hipStream_t stream) {
+  return build_impl(dtype, 1, B, Hkv, D, page_size, ctx_len, q_len, reserve, pol, k_dense,
                     v_dense, free_pages, n_free, n_phys, k_pool, v_pool, seg_table, kv_len, v2p,
                     stream, importance, row_pos);
 }
@@ -746,9 +747,9 @@ sp_status segpaged_append(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int
   if (B < 0 || Hkv < 1 || pol == nullptr) return SP_ERR_INVALID_ARG;
   if (Hkv > kMaxAppendHeads) return SP_ERR_UNSUPPORTED;
   for (int32_t h = 0; h < Hkv; ++h) {
-    if (pol[h].kind == SP_LOCAL_ADAPTIVE || pol[h].kind == SP_RETRIEVAL)
-      return SP_ERR_UNSUPPORTED;
-    if (pol[h].kind != SP_GLOBAL && pol[h].kind != SP_LOCAL) return SP_ERR_INVALID_ARG;
+    if (pol[h].kind == SP_LOCAL_ADAPTIVE) return SP_ERR_UNSUPPORTED;
+    if (pol[h].kind != SP_GLOBAL && pol[h].kind != SP_LOCAL && pol[h].kind != SP_RETRIEVAL)
+      return SP_ERR_INVALID_ARG;
     if (pol[h].kind == SP_LOCAL && (pol[h].sink < 0 || pol[h].window < 1))
       return SP_ERR_INVALID_ARG;
   }

@@ -1412,6 +1412,8 @@ __global__ void __launch_bounds__(64) append_kernel(AppendParams p) {
   }
   const int r0 = max(0, L + 1 - window);  // first window position of the query at L
   int ring = -1;
+  int t = 0;                                // segment that takes the token
+  if (kind == SP_RETRIEVAL) t = own[1] > 0;  // its query chunk; the kept prefix is fixed
   if (kind == SP_LOCAL) {
     if (sink == 0) {
       ring = 0;
@@ -1439,7 +1441,7 @@ __global__ void __launch_bounds__(64) append_kernel(AppendParams p) {
     pos[ring] += k * P;
     ntok[ring] -= k * P;
   }
-  const int t = ring >= 0 ? ring : 0;
+  if (ring >= 0) t = ring;
   const int slot_idx = ntok[t];
   const int page = slot_idx / P;
   if (own[t] < 1 || page >= own[t] || k > own[t] || vs[t] < 0 ||

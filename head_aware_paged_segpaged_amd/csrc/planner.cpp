@@ -148,14 +148,18 @@ int head_segments(const sp_head_policy& pol_in, int32_t L, int32_t q, int32_t ou
   return 2;
 }
 
-sp_status check_growable(int32_t B, const int32_t* ctx_len, const int32_t* reserve, int32_t Hkv,
-                         const sp_head_policy* pol) {
+sp_status check_growable(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                         const int32_t* reserve, int32_t Hkv, const sp_head_policy* pol) {
   if (B > 0 && reserve == nullptr) return SP_ERR_INVALID_ARG;
-  for (int32_t h = 0; h < Hkv; ++h)
-    if (pol[h].kind == SP_LOCAL_ADAPTIVE || pol[h].kind == SP_RETRIEVAL)
-      return SP_ERR_UNSUPPORTED;
+  bool retrieval = false;
+  for (int32_t h = 0; h < Hkv; ++h) {
+    if (pol[h].kind == SP_LOCAL_ADAPTIVE) return SP_ERR_UNSUPPORTED;
+    retrieval |= pol[h].kind == SP_RETRIEVAL;
+  }
   for (int32_t b = 0; b < B; ++b) {
     if (reserve[b] < 0 || (reserve[b] > 0 && ctx_len[b] < 1)) return SP_ERR_INVALID_ARG;
+    // a growing retrieval head appends to its query chunk, which must exist
+    if (retrieval && reserve[b] > 0 && q_len[b] < 1) return SP_ERR_INVALID_ARG;
     if (int64_t(ctx_len[b]) + reserve[b] > kInt32Max) return SP_ERR_UNSUPPORTED;
   }
   return SP_OK;
@@ -167,6 +171,10 @@ void owned_pages(const sp_head_policy& pol, int nseg, const int32_t pos[2],
   if (nseg == 0 || lmax <= L) return;
   if (pol.kind == SP_GLOBAL) {
     own[0] = ceil_div(lmax, P);
+    return;
+  }
+  if (pol.kind == SP_RETRIEVAL) {  // the query chunk (last segment) grows, the kept prefix not
+    own[nseg - 1] = ceil_div(int64_t(ntok[nseg - 1]) + (lmax - L), P);
     return;
   }
   const int64_t W = pol.window, S = pol.sink;

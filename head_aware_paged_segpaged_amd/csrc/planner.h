@@ -65,10 +65,11 @@ sp_status make_layout_layers(int32_t n_layers, int32_t B, const int32_t* ctx_len
                              const int32_t* q_len, int32_t Hkv, const sp_head_policy* pol,
                              int32_t P, const int32_t* reserve, Layout* out);
 
-// Arguments of a growable layout: reserve[b] >= 0, a non-empty context where reserve[b] > 0,
-// no context-adaptive heads (their window moves with the context).
-sp_status check_growable(int32_t B, const int32_t* ctx_len, const int32_t* reserve, int32_t Hkv,
-                         const sp_head_policy* pol);
+// Arguments of a growable layout: reserve[b] >= 0, a non-empty context (and, with retrieval
+// heads, a non-empty query chunk) where reserve[b] > 0, no context-adaptive heads (their
+// window moves with the context).
+sp_status check_growable(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
+                         const int32_t* reserve, int32_t Hkv, const sp_head_policy* pol);
 // Pages owned by each of the nseg segments of one head whose context L may grow to lmax.
 void owned_pages(const sp_head_policy& pol, int nseg, const int32_t pos[2],
                  const int32_t ntok[2], int64_t L, int64_t lmax, int32_t P, int64_t own[2]);

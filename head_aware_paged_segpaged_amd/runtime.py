@@ -196,10 +196,12 @@ class SegPagedDecoder:
         self.seg_table = self.kv_len = self.v2p = None
         self.error = None
         self.workspace = None
+        self.row_pos = None
         self.n_phys = 0
 
     def build(self, k_dense: torch.Tensor, v_dense: torch.Tensor, free_pages,
-              n_phys: int | None = None, stream=None) -> None:
+              n_phys: int | None = None, stream=None, importance=None) -> None:
+        """Layouts with RETRIEVAL heads need ``importance`` (host float32 [T, Hkv])."""
         self.n_phys = int(n_phys if n_phys is not None else max(self.n_virt, 1))
         t = _TORCH[self.dtype]
         self.k_pool = torch.empty((max(self.n_phys, 1), self.P, self.D), dtype=t,
@@ -213,11 +215,19 @@ class SegPagedDecoder:
         self.kv_len = tables[n_tab:n_tab + n_kl].view(Bn, self.Hkv)
         self.v2p = tables[n_tab + n_kl:n_tab + n_kl + max(self.n_virt, 1)]
         self.error = tables[-1:]
-        B.segpaged_build_growable(self.dtype, self.D, self.P, self.ctx_len, self.q_len,
-                                  self.reserve, self.policy, k_dense, v_dense,
-                                  np.asarray(free_pages, dtype=np.int32), self.n_phys,
-                                  self.k_pool, self.v_pool, self.seg_table, self.kv_len,
-                                  self.v2p, stream)
+        fl = np.asarray(free_pages, dtype=np.int32)
+        if importance is not None:
+            n_rows = B.segpaged_retrieval_rows(self.ctx_len, self.q_len, self.policy)
+            self.row_pos = torch.zeros((max(n_rows, 1),), dtype=torch.int32, device=self.device)
+            B.segpaged_build_scored(self.dtype, self.D, self.P, self.ctx_len, self.q_len,
+                                    self.policy, importance, k_dense, v_dense, fl, self.n_phys,
+                                    self.k_pool, self.v_pool, self.seg_table, self.kv_len,
+                                    self.v2p, self.row_pos, stream, reserve=self.reserve)
+        else:
+            B.segpaged_build_growable(self.dtype, self.D, self.P, self.ctx_len, self.q_len,
+                                      self.reserve, self.policy, k_dense, v_dense, fl,
+                                      self.n_phys, self.k_pool, self.v_pool, self.seg_table,
+                                      self.kv_len, self.v2p, stream)
         self.ctx_now = self.ctx_len.copy()
 
     def plan(self, stream=None) -> None:

@@ -65,7 +65,7 @@
  *   prefix the chunk alone. The tables depend only on (L, q, S, p); which tokens fill the first
  *   segment depends on the importance. Every stored token is visible to every query of the
  *   chunk up to the causal edge, so attention reads exactly its stored tokens. Not supported
- *   by the dense-plus-mask path, growable layouts or several layers per build.
+ *   by the dense-plus-mask path or several layers per build.
  * - seg_table int32 [B][Hkv][2][4] = {pos_start, n_tok, vpage_start, n_pages} per segment
  *   slot; an unused slot is {0, 0, running page total, 0}.
  * - Each segment starts on a fresh page; slot i of the segment's k-th page holds position
@@ -218,9 +218,13 @@ sp_status segpaged_build_layers(sp_dtype dtype, int32_t n_layers, int32_t B, int
  *                     are dropped: pos_start += k*P, n_tok -= k*P, and the segment's v2p
  *                     entries rotate left by k (the dropped physical pages move to its end,
  *                     where later tokens reuse them); then the token goes to its end.
+ *   RETRIEVAL         the token goes to the end of its last segment, the query chunk, which
+ *                     owns ceil((q + reserve[b]) / P) pages; its kept prefix never changes (a
+ *                     growing request needs q_len[b] >= 1; layouts with retrieval heads are
+ *                     built by segpaged_build_scored with a reserve).
  * A ring thus keeps at most W + P - 1 tokens; fewer than P of them (all older than the window)
- * are stale, and attention masks them by position. Context-adaptive and retrieval heads are
- * not growable (SP_ERR_UNSUPPORTED).
+ * are stale, and attention masks them by position. Context-adaptive heads are not growable
+ * (SP_ERR_UNSUPPORTED).
  * --------------------------------------------------------------------------------------- */
 
 /* Number of kept-prefix rows of all SP_RETRIEVAL heads (the size of row_pos), in
@@ -232,6 +236,8 @@ sp_status segpaged_retrieval_rows(int32_t B, const int32_t* ctx_len, const int32
  * retrieval heads keep only the top-p important tokens; the selection happens once, at
  * KV-write time, like the rest of the layout). Same arguments and errors as segpaged_build,
  * plus:
+ *   reserve    : host int32 [B] or NULL: with it the layout is the growable one of
+ *                segpaged_build_growable (below), RETRIEVAL heads included
  *   importance : host float [sum(ctx_len)][Hkv], token-major like k_dense; only the prefix
  *                tokens of RETRIEVAL heads are read; a non-finite value there is
  *                SP_ERR_INVALID_ARG.
@@ -242,11 +248,12 @@ sp_status segpaged_retrieval_rows(int32_t B, const int32_t* ctx_len, const int32
  * RETRIEVAL rows, since it has no importance. */
 sp_status segpaged_build_scored(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D,
                                 int32_t page_size, const int32_t* ctx_len, const int32_t* q_len,
-                                const sp_head_policy* pol, const float* importance,
-                                const void* k_dense, const void* v_dense,
-                                const int32_t* free_pages, int64_t n_free, int64_t n_phys,
-                                void* k_pool, void* v_pool, int32_t* seg_table, int32_t* kv_len,
-                                int32_t* v2p, int32_t* row_pos, hipStream_t stream);
+                                const int32_t* reserve, const sp_head_policy* pol,
+                                const float* importance, const void* k_dense,
+                                const void* v_dense, const int32_t* free_pages, int64_t n_free,
+                                int64_t n_phys, void* k_pool, void* v_pool, int32_t* seg_table,
+                                int32_t* kv_len, int32_t* v2p, int32_t* row_pos,
+                                hipStream_t stream);
 
 /* Pages (n_virt) and host tables of the growable layout. reserve: host int32 [B] >= 0; a
  * request with reserve[b] > 0 needs ctx_len[b] >= 1. Errors as segpaged_plan_pages /
@@ -277,7 +284,7 @@ sp_status segpaged_build_growable(sp_dtype dtype, int32_t B, int32_t Hkv, int32_
 /* Appends one token to every request with n_new[b] == 1 (n_new: device int32 [B] of 0 / 1, or
  * NULL for all), following the rules above; one work group per (request, KV head), all state on
  * the device, nothing read back, no host synchronisation.
- *   pol          : host [Hkv], SP_GLOBAL or SP_LOCAL (Hkv <= 128)
+ *   pol          : host [Hkv], SP_GLOBAL, SP_LOCAL or SP_RETRIEVAL (Hkv <= 128)
  *   k_new, v_new : device [B][Hkv][D], row (b, h) is request b's new token for KV head h
  *   k_pool, v_pool, n_phys, seg_table, kv_len, v2p : a growable layout (updated in place)
  *   n_virt       : number of v2p entries (segpaged_plan_pages_growable)

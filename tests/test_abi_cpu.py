@@ -185,7 +185,9 @@ def test_growable_layout_tables_match_oracle():
         q = np.array([rng.integers(1, c + 1) if rng.random() < 0.5 else 1 for c in ctx])
         reserve = rng.integers(0, 2000, size=B) * (rng.random(B) < 0.8)
         pol = [(0, 0, 1) if rng.random() < 0.3 else
-               (1, int(rng.integers(0, 300)), int(rng.integers(1, 1200))) for _ in range(Hkv)]
+               (3, int(rng.integers(0, 30)), int(rng.integers(1, 1001))) if rng.random() < 0.3
+               else (1, int(rng.integers(0, 300)), int(rng.integers(1, 1200)))
+               for _ in range(Hkv)]
         seg, kvl = sp.segpaged_layout_tables_growable(ctx, q, reserve, pol, P)
         seg_o, kvl_o, n_virt = grow_tables(ctx, q, reserve, pol, P)
         np.testing.assert_array_equal(seg, seg_o)
@@ -247,9 +249,9 @@ def test_retrieval_layout_tables_and_invalid_arguments():
     with pytest.raises(sp.SegPagedError) as e:  # the dense-plus-mask path cannot mask it
         sp.segpaged_dense_mask_workspace_size("bf16", 1, 1, 128, [100], [1], pol)
     assert e.value.status == E.SP_ERR_UNSUPPORTED
-    with pytest.raises(sp.SegPagedError) as e:
-        sp.segpaged_plan_pages_growable([100], [1], [4], pol, 64)
-    assert e.value.status == E.SP_ERR_UNSUPPORTED
+    with pytest.raises(sp.SegPagedError) as e:  # growing retrieval heads need a query chunk
+        sp.segpaged_plan_pages_growable([100], [0], [4], pol, 64)
+    assert e.value.status == E.SP_ERR_INVALID_ARG
     lib = binding.lib()
     fake = binding._vp(256)
     c, ql, p = (np.array(x, np.int32) for x in ([100], [1], pol))
@@ -259,7 +261,7 @@ def test_retrieval_layout_tables_and_invalid_arguments():
                               4, 4, fake, fake, fake, fake, fake, None) == E.SP_ERR_INVALID_ARG
     imp = np.ones((100, 1), np.float32)
     imp[50, 0] = np.nan
-    assert lib.segpaged_build_scored(0, 1, 1, 128, 64, binding._ptr(c), binding._ptr(ql),
+    assert lib.segpaged_build_scored(0, 1, 1, 128, 64, binding._ptr(c), binding._ptr(ql), None,
                                      binding._ptr(p), binding._ptr(imp), fake, fake,
                                      binding._ptr(np.arange(4, dtype=np.int32)), 4, 4, fake,
                                      fake, fake, fake, fake, fake, None) == E.SP_ERR_INVALID_ARG

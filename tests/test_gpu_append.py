@@ -15,7 +15,7 @@ import torch
 import oracle
 from head_aware_paged_segpaged_amd import SP_ERR_SEGMENT_FULL, SegPagedDecoder, SegPagedLayer
 from tests.helpers import DEV, MAXABS, COS_MIN, to_device, to_f64
-from workloads import GLOBAL, LOCAL, custom_case, free_list
+from workloads import GLOBAL, LOCAL, RETRIEVAL, custom_case, free_list, importance_scores
 
 pytestmark = pytest.mark.gpu
 
@@ -35,14 +35,14 @@ def _token_rows(x, lengths, pos):
     return np.ascontiguousarray(x[starts + np.asarray(pos)])
 
 
-def _check_pool(dec, st, v2p, case, final_len):
+def _check_pool(dec, st, v2p, case, final_len, keeps=None):
     kp, vp = dec.k_pool.cpu(), dec.v_pool.cpu()
     starts = np.concatenate([[0], np.cumsum(final_len)[:-1]])
     kk = to_device(case.k, case.dtype).cpu()
     vv = to_device(case.v, case.dtype).cpu()
     for b in range(case.B):
         for h in range(case.Hkv):
-            got = oracle.gather_positions(st, v2p, case.P, b, h)
+            got = oracle.gather_positions(st, v2p, case.P, b, h, (keeps or {}).get((b, h)))
             pos = np.array([g[0] for g in got], dtype=np.int64)
             ph = torch.tensor([g[1] for g in got], dtype=torch.long)
             sl = torch.tensor([g[2] for g in got], dtype=torch.long)
@@ -61,14 +61,18 @@ def _cos_maxabs(got, ref):
 
 
 def _run(seed, dtype, Hq, Hkv, D, P, ctx, qb, steps, policy, mask_seed=None, prefill_check=True):
+    # The case's query chunk is the build's chunk followed by the decode steps' queries, so the
+    # oracle sees the same prefix boundary as the build (it decides what RETRIEVAL heads keep).
     ctx, qb = np.asarray(ctx), np.asarray(qb)
     final = ctx + steps
     case = custom_case(seed, dtype=dtype, Hq=Hq, Hkv=Hkv, D=D, P=P, ctx_len=final,
-                       q_len=np.full(len(ctx), steps), policy=policy, name="append")
+                       q_len=qb + steps, policy=policy, name="append")
     print("case append seed", seed, dtype, "P", P, "ctx", ctx.tolist(), "q", qb.tolist(),
           "steps", steps, "policy", np.asarray(policy).tolist(), flush=True)
-    ref = oracle.attention(case.q, case.k, case.v, final, np.full(len(ctx), steps), case.policy,
-                           Hq, Hkv, case.scale, dtype)
+    retrieval = bool((case.policy[:, 0] == RETRIEVAL).any())
+    imp = importance_scores(case) if retrieval else None
+    ref = oracle.attention(case.q, case.k, case.v, final, qb + steps, case.policy, Hq, Hkv,
+                           case.scale, dtype, importance=imp)
     k_build = to_device(_split_rows(case.k, final, ctx), dtype)
     v_build = to_device(_split_rows(case.v, final, ctx), dtype)
     reserve = np.full(len(ctx), steps)
@@ -77,8 +81,17 @@ def _run(seed, dtype, Hq, Hkv, D, P, ctx, qb, steps, policy, mask_seed=None, pre
     assert dec.n_virt == nv
     n_phys = nv + 7
     fl = free_list(seed, n_phys)
-    dec.build(k_build, v_build, fl, n_phys=n_phys)
+    imp_build = _split_rows(imp, final, ctx) if retrieval else None
+    dec.build(k_build, v_build, fl, n_phys=n_phys, importance=imp_build)
     v2p = fl[:nv].copy()
+    keeps, row0 = {}, 0
+    for b in range(len(ctx)):
+        for h in range(Hkv):
+            kind, sink, window = (int(x) for x in case.policy[h])
+            if kind == RETRIEVAL and ctx[b] - qb[b] > 0:
+                keeps[(b, h)] = oracle.retrieval_keep(imp_build[row0:row0 + ctx[b], h], sink,
+                                                      window, int(ctx[b]), int(qb[b]))
+        row0 += int(ctx[b])
     np.testing.assert_array_equal(dec.seg_table.cpu().numpy(), st)
     np.testing.assert_array_equal(dec.kv_len.cpu().numpy(), kl)
     if prefill_check:
@@ -91,13 +104,13 @@ def _run(seed, dtype, Hq, Hkv, D, P, ctx, qb, steps, policy, mask_seed=None, pre
         got = to_f64(layer.attention(to_device(pre.q, dtype), pre.scale))
         exp = oracle.attention(pre.q, _split_rows(case.k, final, ctx),
                                _split_rows(case.v, final, ctx), ctx, qb, case.policy, Hq, Hkv,
-                               pre.scale, dtype)
+                               pre.scale, dtype, importance=imp_build)
         assert float(np.abs(got - exp).max()) <= MAXABS[dtype]
         assert layer.check() == 0
     dec.plan()
     rng = np.random.default_rng(mask_seed) if mask_seed is not None else None
     count = np.zeros(len(ctx), dtype=np.int64)
-    q_rows = np.arange(len(ctx)) * steps
+    q_rows = np.concatenate([[0], np.cumsum(qb + steps)[:-1]]) + qb
     worst = (0.0, 1.0)
     for t in range(steps):
         n_new = None
@@ -120,7 +133,7 @@ def _run(seed, dtype, Hq, Hkv, D, P, ctx, qb, steps, policy, mask_seed=None, pre
             m, c = _cos_maxabs(out[b], ref[rows[b]])
             worst = (max(worst[0], m), min(worst[1], c))
     assert dec.check() == (0, 0)
-    _check_pool(dec, st, v2p, case, final)
+    _check_pool(dec, st, v2p, case, final, keeps)
     print("append %s steps %d: maxabs=%.3e min_cos=%.8f" % (dtype, steps, *worst), flush=True)
     assert worst[0] <= MAXABS[dtype] and worst[1] > COS_MIN
     return dec
@@ -142,6 +155,14 @@ def test_append_with_idle_requests():
 
 def test_append_fp32_d64():
     _run(730, "f32", 4, 2, 64, 32, [50, 400], [1, 100], 70, [(LOCAL, 3, 40), (GLOBAL, 0, 1)])
+
+
+@pytest.mark.parametrize("P", [16, 64])
+def test_append_with_retrieval_heads(P):
+    # RETRIEVAL heads grow through their query chunk while LOCAL rings recycle and GLOBAL heads
+    # grow beside them; one request is built from a long prefill chunk, one from a decode query
+    pol = [(RETRIEVAL, 4, 150), (LOCAL, 4, 60), (GLOBAL, 0, 1), (RETRIEVAL, 0, 1)]
+    _run(790 + P, "bf16", 8, 4, 128, P, [700, 2500, 90], [200, 1, 90], 60, pol)
 
 
 def test_append_long_ring_rotation():
