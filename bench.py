@@ -408,7 +408,7 @@ def main() -> int:
     if args.decode_steps > 0:
         line["decode_append"] = decode_append_leg(args, case, k, v, up, evict, stream, ms_step,
                                                   SegPagedDecoder, HipEvent, decode_tokens,
-                                                  free_list)
+                                                  free_list, importance)
     if args.build_layers > 0:
         del layer
         line["build_layers"] = build_layers_leg(args.build_layers, case, k, v, evict, stream,
@@ -425,15 +425,15 @@ def main() -> int:
 
 
 def decode_append_leg(args, case, k, v, up, evict, stream, planned_ms, decoder_cls, event_cls,
-                      decode_tokens, free_list) -> dict:
+                      decode_tokens, free_list, importance=None) -> dict:
     """Decode with growth: the workload's context built into a growable layout (pages reserved
     for the steps to come), then warmup + N steps, each appending every request's new token
     and running the table-driven decode on it. Timed with HIP events on the stream: the whole
     loop, and every EVENT_EVERY-th append."""
     import torch
-    if int(case.q_len.max()) != 1 or (case.policy[:, 0] >= 2).any():
+    if int(case.q_len.max()) != 1 or (case.policy[:, 0] == 2).any():
         return {"skipped": "needs a decode workload (one query per request) without "
-                           "context-adaptive or retrieval heads"}
+                           "context-adaptive heads"}
     n_steps, n_warm = args.decode_steps, args.warmup
     total = n_steps + 2 * n_warm
     R = case.B if args.decode_requests <= 0 else min(args.decode_requests, case.B)
@@ -445,10 +445,11 @@ def decode_append_leg(args, case, k, v, up, evict, stream, planned_ms, decoder_c
     reserve = np.full(R, total + n_steps, dtype=np.int32)
     dec = decoder_cls(case.dtype, case.Hq, case.Hkv, case.D, case.P, ctx, ql, reserve,
                       case.policy, k.device)
-    dec.build(k, v, free_list(case.seed, dec.n_virt))
+    dec.build(k, v, free_list(case.seed, dec.n_virt),
+              importance=importance[:rows] if importance is not None else None)
     dec.plan()
     out = torch.empty_like(qn[0])
-    local = case.policy[:, 0] != 0
+    local = case.policy[:, 0] == 1
 
     def rows_of():
         kl = dec.kv_len.cpu().numpy().astype(np.int64)
@@ -515,7 +516,7 @@ def decode_append_leg(args, case, k, v, up, evict, stream, planned_ms, decoder_c
             "append_ms": round(append_ms, 5), "tokens_per_s": round(R / (ms * 1e-3), 1),
             "decode_gbps": round(gbps, 1), "decode_hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
             "vs_planned_step": round(ms / planned_ms, 3) if R == case.B else None,
-            "local_rows": [rows0[0], rows1[0]], "global_rows": [rows0[1], rows1[1]],
+            "local_rows": [rows0[0], rows1[0]], "other_rows": [rows0[1], rows1[1]],
             "pages_owned": int(dec.n_virt), "graph": graph}
 
 
