@@ -4,7 +4,8 @@
  * Method (page "RedKnot SegPagedAttention runtime design", sections 1-4): every KV head owns
  * its own page table over one shared physical page pool. A GLOBAL head stores and reads the
  * whole context. A LOCAL head stores and reads only its first S "sink" tokens plus a recent
- * window of W tokens. Attention then packs every (query head, KV head) pair into one
+ * window of W tokens. A RETRIEVAL head stores its sink, the most important part of its prefix
+ * and its query chunk. Attention then packs every (query head, KV head) pair into one
  * variable-length launch in which each head walks only its own stored pages, so LOCAL heads
  * neither hold nor move KV they cannot see.
  *
@@ -12,11 +13,14 @@
  *   segpaged_plan_pages           host only: how many pages a layout needs
  *   segpaged_layout_tables        host only: the tables segpaged_build will write
  *   segpaged_build                once per layout: page tables + fill the pool from dense K/V
+ *                                 (segpaged_build_scored when RETRIEVAL heads need importance;
+ *                                 segpaged_build_layers for several layers in one pool)
  *   segpaged_attention_workspace_size / segpaged_attention_plan
  *                                 once per layout: the work list the attention kernels pop
  *   segpaged_attention            every call: O = attention(Q, paged K/V)
  * Decode over a layout that grows by one token per step:
  *   segpaged_build_growable       once: the layout with pages reserved for decode tokens
+ *                                 (segpaged_build_scored with a reserve for RETRIEVAL heads)
  *   segpaged_decode_workspace_size / segpaged_decode_plan
  *                                 once (re-plan at will): a work list that reads lengths from
  *                                 the device tables when it runs
