@@ -1444,10 +1444,12 @@ __global__ void __launch_bounds__(64) append_kernel(AppendParams p) {
   if (ring >= 0) t = ring;
   const int slot_idx = ntok[t];
   const int page = slot_idx / P;
-  if (own[t] < 1 || page >= own[t] || k > own[t] || vs[t] < 0 ||
-      int64_t(vs[t]) + own[t] > p.n_virt) {
-    append_error(p.error, own[t] >= 1 && page >= own[t] ? SP_ERR_SEGMENT_FULL
-                                                         : SP_ERR_INVALID_ARG);
+  if (own[t] < 0 || k > own[t] || vs[t] < 0 || int64_t(vs[t]) + own[t] > p.n_virt) {
+    append_error(p.error, SP_ERR_INVALID_ARG);
+    return;
+  }
+  if (page >= own[t]) {  // no owned page left for the token (appending past the reserve)
+    append_error(p.error, SP_ERR_SEGMENT_FULL);
     return;
   }
   // Physical page of the new token, read before the rotation: after rotating left by k,
