@@ -265,3 +265,18 @@ def test_retrieval_layout_tables_and_invalid_arguments():
                                      binding._ptr(p), binding._ptr(imp), fake, fake,
                                      binding._ptr(np.arange(4, dtype=np.int32)), 4, 4, fake,
                                      fake, fake, fake, fake, fake, None) == E.SP_ERR_INVALID_ARG
+
+
+def test_layers_build_rejects_retrieval_heads():
+    # the several-layer build takes no importance, so layouts that keep RETRIEVAL rows are
+    # rejected before anything is queued (the layout queries still describe them)
+    lib = binding.lib()
+    fake = binding._vp(256)
+    c, ql = np.array([100], np.int32), np.array([1], np.int32)
+    pol = np.array([[(3, 4, 100)], [(0, 0, 1)]], np.int32)
+    n = sp.segpaged_plan_pages_layers([100], [1], pol, 64)
+    fl = np.arange(n, dtype=np.int32)
+    assert lib.segpaged_build_layers(0, 2, 1, 1, 128, 64, binding._ptr(c), binding._ptr(ql),
+                                     binding._ptr(pol), fake, fake, binding._ptr(fl), n, n,
+                                     fake, fake, fake, fake, fake, None) == \
+        binding.SP_ERR_INVALID_ARG
