@@ -1,6 +1,6 @@
 """Benchmark of head-aware SegPaged attention on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I]   (default I = 2)
 
 One step = one segpaged_attention call (the persistent prefill or decode kernel plus the
 fixed-order combine) over the workload's batch, with the layout already built and the work
@@ -153,11 +153,12 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=1,
+    ap.add_argument("--config", type=int, default=2,
                     help="workload index (0-7; 5 = the 32K-128K slice of the decode workload, "
                          "6 = the decode workload with context-adaptive LOCAL windows, "
-                         "7 = the decode workload with two RETRIEVAL heads); "
-                         "default 1")
+                         "7 = the decode workload with two RETRIEVAL heads); default 2, the "
+                         "Llama-3.3-70B-shaped layer (batch 4, 2048-token chunks of 16K-32K "
+                         "contexts), the largest workload that runs on one GPU")
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="rows of the CPU-oracle sample (default sized for about 10-30 s)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense+mask timing")

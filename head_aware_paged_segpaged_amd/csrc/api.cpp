@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -69,6 +70,47 @@ sp_status workspace_size(const Shape& s, size_t* bytes) {
   return SP_OK;
 }
 
+// Combine items of recently planned shapes, by plan signature. segpaged_attention skips the
+// combine launch for a signature planned here with no KV-split item. The plan is a function
+// of what the signature hashes (shapes, lengths, policies, grid sizes), so an entry never goes
+// stale; a signature not found here (evicted, or planned in another process) launches the
+// combine, whose kernel reads the item count from the workspace and returns at once.
+class CombineCounts {
+ public:
+  void put(uint64_t sig, int32_t n) {
+    std::lock_guard<std::mutex> g(mu_);
+    for (Entry& e : ent_)
+      if (e.used && e.sig == sig) {
+        e.n = n;
+        return;
+      }
+    ent_[next_] = Entry{sig, n, true};
+    next_ = (next_ + 1) % kEntries;
+  }
+  bool zero(uint64_t sig) {
+    std::lock_guard<std::mutex> g(mu_);
+    for (const Entry& e : ent_)
+      if (e.used && e.sig == sig) return e.n == 0;
+    return false;
+  }
+
+ private:
+  static constexpr int kEntries = 64;
+  struct Entry {
+    uint64_t sig;
+    int32_t n;
+    bool used;
+  };
+  std::mutex mu_;
+  Entry ent_[kEntries] = {};
+  int next_ = 0;
+};
+
+CombineCounts& combine_counts() {
+  static CombineCounts c;
+  return c;
+}
+
 sp_status plan_into(const Shape& s, void* workspace, size_t ws_bytes, hipStream_t stream) {
   sp_status st = check_shape(s);
   if (st != SP_OK) return st;
@@ -86,6 +128,7 @@ sp_status plan_into(const Shape& s, void* workspace, size_t ws_bytes, hipStream_
       hipSuccess)
     return SP_ERR_HIP;
   if (hipStreamSynchronize(stream) != hipSuccess) return SP_ERR_HIP;
+  combine_counts().put(plan.hdr.signature, plan.hdr.n_combine);
   return SP_OK;
 }
 
@@ -142,6 +185,7 @@ sp_status run_attention(const Shape& s, const void* q, const void* k, const void
   if (need_dec && launch_attention(s.dtype, s.D, s.mode, true, gd, p, stream) != hipSuccess)
     return SP_ERR_HIP;
   if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return SP_ERR_HIP;
+  if (combine_counts().zero(p.signature)) return SP_OK;
   int cus = 0;
   st = device_cus(&cus);
   if (st != SP_OK) return st;
@@ -380,6 +424,9 @@ sp_status table_decode_shape(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
   *s = make_shape(kModePaged, dtype, B, Hq, Hkv, D, P, hint->data(), ones->data(), pol);
   sp_status st = check_shape(*s);
   if (st != SP_OK) return st;
+  // A decode item holds the G query heads of one KV head as its rows (at most kDecodeRows);
+  // larger groups would be planned as prefill items, which this call never launches.
+  if (Hq / Hkv > kDecodeRows) return SP_ERR_UNSUPPORTED;
   for (int32_t h = 0; h < Hkv; ++h)
     if (pol[h].kind == SP_LOCAL_ADAPTIVE) return SP_ERR_UNSUPPORTED;
   return SP_OK;

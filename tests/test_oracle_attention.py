@@ -253,3 +253,25 @@ def test_adaptive_window_divisor_one_equals_global():
     oa = attention(a.q, a.k, a.v, a.ctx_len, a.q_len, a.policy, 2, 1, a.scale, a.dtype)
     ob = attention(b.q, b.k, b.v, b.ctx_len, b.q_len, b.policy, 2, 1, b.scale, b.dtype)
     np.testing.assert_array_equal(oa, ob)
+
+
+def test_bf16_conversion_every_bit_pattern():
+    """oracle.to_f64 against torch's own bf16 -> float64 conversion on all 65,536 bf16 bit
+    patterns (NaN patterns must stay NaN). Every bf16 pin above converts its inputs and its
+    reference through to_f64, so this is what ties those pins to the bf16 format itself."""
+    from oracle import to_f64
+
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = to_f64(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * 127  # exponent all ones with a non-zero 7-bit mantissa, both signs
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zeros and infinities keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    # a few values worked out by hand from the format (sign, 8-bit exponent, 7-bit mantissa)
+    assert got[0x3F80] == 1.0 and got[0xC000] == -2.0 and got[0x3F40] == 0.75
+    assert got[0x0001] == 2.0 ** -133  # smallest subnormal: 2^-126 * 2^-7
+    assert got[0x7F7F] == (2.0 - 2.0 ** -7) * 2.0 ** 127  # largest finite
+    assert np.isinf(got[0x7F80]) and got[0xFF80] < 0
