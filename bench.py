@@ -173,6 +173,12 @@ def main() -> int:
                     help="no GPU run: turn two rocprofv3 --pmc runs of this workload "
                          "(FETCH_SIZE, then WRITE_SIZE, each with --copy-calibration) into "
                          "HBM bytes per launch of its main kernel in profiles/traffic.json")
+    ap.add_argument("--counters-from", nargs="+", metavar="PMC_DIR",
+                    help="no GPU run: average every counter of these rocprofv3 --pmc run "
+                         "directories over the dispatches of this workload's main kernel and "
+                         "store them in profiles/counters.json (with the MFMA busy share, the "
+                         "bf16 MFMA FLOPs per dispatch against the visible-pair FLOPs, and the "
+                         "per-wave instruction counts per KV step)")
     ap.add_argument("--build-layers", type=int, default=0, metavar="N",
                     help="also time one build of N layers of this workload's shape into one "
                          "shared page pool (layer l's KV-head policies are the workload's "
@@ -193,6 +199,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.traffic_from:
         return write_traffic(args)
+    if args.counters_from:
+        return write_counters(args)
     if args.gemm_reference:
         return gemm_reference()
     if args.gpus != 1:
@@ -587,6 +595,60 @@ def gemm_reference() -> int:
         ms = (time.perf_counter() - t0) * 1e3 / iters
         out[str(n)] = round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
     print(json.dumps({"bf16_gemm_tflops": out, "peak": PEAK_BF16_TFLOPS}), flush=True)
+    return 0
+
+
+def _main_kernel_counters(d: str, kernel: str) -> dict:
+    """Mean of every counter over the paged-mode dispatches of `kernel` in one --pmc run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under " + d)
+    vals = {}
+    for r in csv.DictReader(open(files[0])):
+        n = r["Kernel_Name"]
+        if kernel + "<" in n and ", 0>" in n:
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit("%s: no %s dispatch in %s" % (kernel, kernel, d))
+    return {k: float(np.mean(v)) for k, v in vals.items()}
+
+
+def write_counters(args) -> int:
+    """Per-dispatch counter means of the workload's main kernel, plus what they imply: the
+    matrix-core busy share (MfmaUtil), bf16 MFMA FLOPs per dispatch against the FLOPs of the
+    visible (query, key) pairs, and instruction counts per wave and 64-key KV step."""
+    from workloads import config_case
+    case = config_case(args.config, with_tensors=False)
+    decode = bool((case.q_len * (case.Hq // case.Hkv) <= 16).all())
+    kernel = "decode_kernel" if decode else "prefill_kernel"
+    counters = {}
+    for d in args.counters_from:
+        counters.update(_main_kernel_counters(d, kernel))
+    rec = {"kernel": kernel, "counters": {k: round(v, 3) for k, v in sorted(counters.items())}}
+    flops = 4.0 * case.D * visible_counts(case).sum() * (case.Hq // case.Hkv)
+    rec["visible_flops_per_launch"] = flops
+    if "MfmaFlopsBF16" in counters:
+        rec["mfma_bf16_flops_per_launch"] = counters["MfmaFlopsBF16"]
+        rec["mfma_flops_over_visible"] = round(counters["MfmaFlopsBF16"] / flops, 4)
+    if "MfmaUtil" in counters:
+        rec["mfma_busy_pct"] = round(counters["MfmaUtil"], 2)
+    if "SQ_WAVES" in counters and "SQ_INSTS_MFMA" in counters and not decode:
+        # every prefill wave issues 32 bf16 MFMAs (32x32x16) per 64-key step
+        steps = counters["SQ_INSTS_MFMA"] / 32.0
+        rec["per_wave_step"] = {k[len("SQ_INSTS_"):].lower(): round(counters[k] / steps, 1)
+                                for k in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
+                                          "SQ_INSTS_MFMA", "SQ_INSTS_VALU_TRANS_F32")
+                                if k in counters}
+    rec["source_hash"] = source_hash()
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data.setdefault(case.name, {})[kernel] = rec
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({case.name: rec}))
     return 0
 
 
