@@ -34,7 +34,8 @@ Parity status: every function here is pinned by tests under ``tests/test_oracle_
 example). Nothing here is "parity unpinned".
 """
 
-from .attention import GLOBAL, LOCAL, attention, attention_rows, to_f64, visible  # noqa: F401
+from .attention import (GLOBAL, LOCAL, attention, attention_group_rows,  # noqa: F401
+                        attention_rows, to_f64, visible)
 from .plan import (LOCAL_ADAPTIVE, RETRIEVAL, gather_positions, head_policy,  # noqa: F401
                    plan_tables, plan_tables_layers, retrieval_counts, retrieval_keep, segments)
 from .append import append_step, grow_tables, owned_pages  # noqa: F401

@@ -107,6 +107,37 @@ def attention_rows(q, k, v, ctx_len, q_len, policy, Hq: int, Hkv: int, scale: fl
                       L - nq)
 
 
+def attention_group_rows(q, k, v, ctx_len, q_len, policy, Hq: int, Hkv: int, scale: float,
+                         dtype: str, b: int, h: int, tokens=None,
+                         importance=None) -> np.ndarray:
+    """O[b, tokens, hq] for every query head hq of KV head h's group, float64, shape
+    [G, len(tokens), D]. The same rows as ``attention_rows`` called once per query head
+    hq = h*G .. h*G+G-1; the group's K/V (and kept set) are converted once for all of them."""
+    ctx_len = np.asarray(ctx_len, dtype=np.int64)
+    q_len = np.asarray(q_len, dtype=np.int64)
+    G = Hq // Hkv
+    L = int(ctx_len[b])
+    nq = int(q_len[b])
+    kv0 = int(ctx_len[:b].sum())
+    q0 = int(q_len[:b].sum())
+    if tokens is None:
+        tokens = np.arange(nq)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    kind, sink, window = head_policy(*(int(x) for x in policy[h]), L)
+    k_head = to_f64(k[kv0:kv0 + L, h, :], dtype)
+    v_head = to_f64(v[kv0:kv0 + L, h, :], dtype)
+    positions = L - nq + tokens
+    kept = None
+    if kind == RETRIEVAL:
+        kept = retrieval_keep(importance[kv0:kv0 + L, h], sink, window, L, nq)
+    out = np.empty((G, len(tokens), v.shape[-1]), dtype=np.float64)
+    for g in range(G):
+        q_rows = to_f64(q[q0 + tokens, h * G + g, :], dtype)
+        out[g] = _head_rows(q_rows, positions, k_head, v_head, kind, sink, window, scale, kept,
+                            L - nq)
+    return out
+
+
 def attention(q, k, v, ctx_len, q_len, policy, Hq: int, Hkv: int, scale: float,
               dtype: str, importance=None) -> np.ndarray:
     """Full O [sum(q_len), Hq, D] in float64."""

@@ -275,3 +275,24 @@ def test_bf16_conversion_every_bit_pattern():
     assert got[0x0001] == 2.0 ** -133  # smallest subnormal: 2^-126 * 2^-7
     assert got[0x7F7F] == (2.0 - 2.0 ** -7) * 2.0 ** 127  # largest finite
     assert np.isinf(got[0x7F80]) and got[0xFF80] < 0
+
+
+def test_group_rows_equal_per_head_rows():
+    """attention_group_rows (one K/V conversion for a whole GQA group) returns exactly the rows
+    attention_rows computes per query head, for every head kind (bitwise: same arithmetic)."""
+    from oracle import attention_group_rows
+    from workloads import LOCAL_ADAPTIVE, RETRIEVAL
+    rng = np.random.default_rng(77)
+    pol = [(GLOBAL, 0, 1), (LOCAL, 4, 40), (LOCAL_ADAPTIVE, 2, 3), (RETRIEVAL, 4, 300)]
+    c = custom_case(77, dtype="bf16", Hq=8, Hkv=4, D=64, P=16, ctx_len=[300, 97],
+                    q_len=[50, 97], policy=pol)
+    imp = rng.standard_normal((int(np.sum(c.ctx_len)), c.Hkv)).astype(np.float32)
+    for b in range(c.B):
+        toks = np.sort(rng.choice(int(c.q_len[b]), 9, replace=False))
+        for h in range(c.Hkv):
+            grp = attention_group_rows(c.q, c.k, c.v, c.ctx_len, c.q_len, c.policy, c.Hq, c.Hkv,
+                                       c.scale, c.dtype, b, h, toks, importance=imp)
+            for g in range(c.Hq // c.Hkv):
+                one = attention_rows(c.q, c.k, c.v, c.ctx_len, c.q_len, c.policy, c.Hq, c.Hkv,
+                                     c.scale, c.dtype, b, h * 2 + g, toks, importance=imp)
+                assert np.array_equal(grp[g], one)
