@@ -92,3 +92,69 @@ def sample_rows(case, budget_rows: int, seed: int = 4321):
         out.append((b, hq, toks))
         rows += len(toks)
     return out
+
+
+def boundary_tokens(nq: int, bq: int, n: int, rng) -> np.ndarray:
+    """Up to n query tokens of a chunk of nq: the first and last token, the two tokens on each
+    side of the first, middle and last query-block boundaries (blocks of bq tokens), then
+    seeded random ones."""
+    pick = {0, nq - 1}
+    nb = (nq + bq - 1) // bq
+    for blk in sorted({1, nb // 2, nb - 1}):
+        if 0 < blk < nb:
+            pick.update((blk * bq - 1, blk * bq))
+    pick = {t for t in pick if 0 <= t < nq}
+    rest = np.setdiff1d(np.arange(nq), np.array(sorted(pick)))
+    extra = max(0, min(n - len(pick), len(rest)))
+    if extra:
+        pick.update(int(t) for t in rng.choice(rest, extra, replace=False))
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def group_parity(case, got: np.ndarray, groups, importance=None, q=None, k=None, v=None,
+                 ctx_len=None, q_len=None, q_row0=None, label=""):
+    """Oracle rows for every (request, KV head, tokens) in `groups` (all query heads of the
+    group), computed on host threads, against the GPU output `got` [rows, Hq, D].
+
+    Returns (max abs error, min cosine over (request, query head), number of rows); the
+    cosine of a (request, query head) is taken over all of its compared rows."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    q = case.q if q is None else q
+    k = case.k if k is None else k
+    v = case.v if v is None else v
+    ctx_len = case.ctx_len if ctx_len is None else ctx_len
+    q_len = case.q_len if q_len is None else q_len
+    if q_row0 is None:
+        q_row0 = np.concatenate([[0], np.cumsum(q_len)[:-1]])
+    G = case.Hq // case.Hkv
+
+    def one(g):
+        b, h, toks = g
+        ref = oracle.attention_group_rows(q, k, v, ctx_len, q_len, case.policy, case.Hq,
+                                          case.Hkv, case.scale, case.dtype, b, h, toks,
+                                          importance=importance)
+        res = []
+        for j in range(G):
+            gg = got[q_row0[b] + toks, h * G + j, :]
+            err = float(np.abs(gg - ref[j]).max()) if gg.size else 0.0
+            na, nb = np.linalg.norm(gg), np.linalg.norm(ref[j])
+            cos = 1.0 if na == 0 and nb == 0 else float(gg.ravel() @ ref[j].ravel() / (na * nb))
+            res.append((err, cos, len(toks)))
+        return b, h, res
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    worst_abs, worst_cos, rows, worst_at = 0.0, 1.0, 0, None
+    with ThreadPoolExecutor(workers) as ex:
+        for b, h, res in ex.map(one, groups):
+            for j, (err, cos, n) in enumerate(res):
+                worst_abs = max(worst_abs, err)
+                if cos < worst_cos:
+                    worst_cos, worst_at = cos, (b, h * G + j)
+                rows += n
+    print("%s %s: %d rows over %d (request, query head) pairs: maxabs=%.3e min_cos=%.8f at %s"
+          % (case.name, label, rows, len(groups) * G, worst_abs, worst_cos, worst_at),
+          flush=True)
+    return worst_abs, worst_cos, rows

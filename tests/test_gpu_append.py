@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from head_aware_paged_segpaged_amd import SP_ERR_SEGMENT_FULL, SegPagedDecoder, SegPagedLayer
-from tests.helpers import DEV, MAXABS, COS_MIN, to_device, to_f64
+from tests.helpers import COS_MIN, DEV, MAXABS, group_parity, to_device, to_f64
 from workloads import GLOBAL, LOCAL, RETRIEVAL, custom_case, free_list, importance_scores
 
 pytestmark = pytest.mark.gpu
@@ -223,11 +223,11 @@ def test_append_past_the_reserve_reports_segment_full():
 
 
 @pytest.mark.parametrize("index", [3, 5])
-def test_full_size_decode_append_sampled(index):
+def test_full_size_decode_append_all_rows(index):
     # The full decode workload (64 requests, 4K-128K contexts, or its 32K+ slice) built into a
     # growable layout, then 16 decode steps, each appending a token per request: tables
-    # bit-exact against the append oracle after every step, and seeded sampled rows of the
-    # last step's output against the dense oracle over the grown contexts.
+    # bit-exact against the append oracle after every step, and every row of the last
+    # step's output against the dense oracle over the grown contexts.
     from workloads import config_case, decode_tokens
     c = config_case(index)
     n = 16
@@ -250,20 +250,18 @@ def test_full_size_decode_append_sampled(index):
     np.testing.assert_array_equal(dec.v2p.cpu().numpy(), v2p)
     assert dec.check() == (0, 0)
     got = to_f64(out)
-    rng = np.random.default_rng(100 + index)
-    worst_abs, worst_cos = 0.0, 1.0
-    for _ in range(12):
-        b, hq = int(rng.integers(c.B)), int(rng.integers(c.Hq))
-        kv0, L = int(c.ctx_len[:b].sum()), int(c.ctx_len[b])
-        k_b = np.concatenate([c.k[kv0:kv0 + L], kn[:, b]])
-        v_b = np.concatenate([c.v[kv0:kv0 + L], vn[:, b]])
-        ref = oracle.attention_rows(qn[n - 1, b][None], k_b, v_b, [L + n], [1], c.policy, c.Hq,
-                                    c.Hkv, c.scale, c.dtype, 0, hq)[0]
-        g = got[b, hq]
-        worst_abs = max(worst_abs, float(np.abs(g - ref).max()))
-        worst_cos = min(worst_cos, float(g @ ref / (np.linalg.norm(g) * np.linalg.norm(ref))))
-    print("%s append sampled: maxabs=%.3e min_cos=%.8f" % (c.name, worst_abs, worst_cos),
-          flush=True)
+    # every row of the last step (one query per (request, query head)) against the dense
+    # oracle over the grown contexts: each request's context followed by its n new tokens
+    row0 = np.concatenate([[0], np.cumsum(c.ctx_len)[:-1]])
+    k_all = np.concatenate([x for b in range(c.B) for x in
+                            (c.k[row0[b]:row0[b] + c.ctx_len[b]], kn[:, b])])
+    v_all = np.concatenate([x for b in range(c.B) for x in
+                            (c.v[row0[b]:row0[b] + c.ctx_len[b]], vn[:, b])])
+    groups = [(b, h, np.array([0])) for b in range(c.B) for h in range(c.Hkv)]
+    worst_abs, worst_cos, rows = group_parity(
+        c, got, groups, q=qn[n - 1], k=k_all, v=v_all, ctx_len=c.ctx_len + n,
+        q_len=np.ones(c.B, dtype=np.int64), q_row0=np.arange(c.B), label="append, last step")
+    assert rows == c.B * c.Hq
     assert worst_abs <= MAXABS[c.dtype] and worst_cos > COS_MIN
 
 

@@ -10,8 +10,8 @@ import pytest
 import torch
 
 import oracle
-from tests.helpers import (COS_MIN, DEV, MAXABS, assert_parity, run_dense_mask, run_segpaged,
-                           sample_rows, to_device, to_f64)
+from tests.helpers import (COS_MIN, DEV, MAXABS, assert_parity, boundary_tokens, group_parity,
+                           run_dense_mask, run_segpaged, to_device, to_f64)
 from workloads import GLOBAL, LOCAL, LOCAL_ADAPTIVE, config_case, custom_case, free_list
 
 pytestmark = pytest.mark.gpu
@@ -235,11 +235,15 @@ def test_decode_repeat_is_bitwise_identical():
     assert layer.check() == 0
 
 
-@pytest.mark.parametrize("index,budget", [(2, 48), (3, 24), (4, 24), (5, 16), (6, 16)])
-def test_full_size_workload_sampled_rows(index, budget):
+@pytest.mark.parametrize("index", [2, 3, 4, 5, 6])
+def test_full_size_every_head(index):
     # The full workloads, planned for this device exactly as the benchmark runs them: page
-    # tables bit-exact, two heads' pool pages bit-exact, and seeded sampled output rows against
-    # the oracle (the whole output is too large for the fp64 oracle).
+    # tables bit-exact, two heads' pool pages bit-exact, and output rows of EVERY (request,
+    # query head) against the oracle. Prefill workloads: 16 query tokens per (request, query
+    # head), among them the chunk's first and last token and the tokens on both sides of
+    # query-block boundaries, plus every row of two complete heads (a GLOBAL and a LOCAL one
+    # of the longest request); decode workloads: all rows. The cosine is per (request, query
+    # head) over its compared rows.
     c = config_case(index)
     print("case full-size", c.name, flush=True)
     out, layer = run_segpaged(c)
@@ -258,18 +262,28 @@ def test_full_size_workload_sampled_rows(index, budget):
         np.testing.assert_array_equal(kp.cpu().view(torch.int16).numpy(), c.k[base + pos, h].view(np.int16))
         np.testing.assert_array_equal(vp.cpu().view(torch.int16).numpy(), c.v[base + pos, h].view(np.int16))
     got = to_f64(out)
-    q_row0 = np.concatenate([[0], np.cumsum(c.q_len)[:-1]])
-    worst_abs, worst_cos = 0.0, 1.0
-    for b, hq, toks in sample_rows(c, budget):
-        ref = oracle.attention_rows(c.q, c.k, c.v, c.ctx_len, c.q_len, c.policy, c.Hq, c.Hkv,
-                                    c.scale, c.dtype, b, hq, toks)
-        g = got[q_row0[b] + toks, hq, :]
-        worst_abs = max(worst_abs, float(np.abs(g - ref).max()))
-        cos = float(g.ravel() @ ref.ravel() / (np.linalg.norm(g) * np.linalg.norm(ref)))
-        worst_cos = min(worst_cos, cos)
-    print("%s sampled: maxabs=%.3e min_cos=%.8f" % (c.name, worst_abs, worst_cos), flush=True)
+    G = c.Hq // c.Hkv
+    bq = max(1, 128 // G)  # query tokens of one prefill work item
+    groups = [(b, h, boundary_tokens(int(c.q_len[b]), bq, 16, rng))
+              for b in range(c.B) for h in range(c.Hkv) if c.q_len[b] > 0]
+    worst_abs, worst_cos, rows = group_parity(c, got, groups, label="every head")
+    assert rows >= min(16, int(c.q_len.min())) * c.B * c.Hq
     assert worst_abs <= MAXABS[c.dtype]
     assert worst_cos > COS_MIN
+    if int(c.q_len.max()) > 1:
+        q_row0 = np.concatenate([[0], np.cumsum(c.q_len)[:-1]])
+        b = int(np.argmax(c.ctx_len))
+        for kind in (G_, L_):
+            h = int(np.nonzero(c.policy[:, 0] == kind)[0][0])
+            ref = oracle.attention_rows(c.q, c.k, c.v, c.ctx_len, c.q_len, c.policy, c.Hq,
+                                        c.Hkv, c.scale, c.dtype, b, h * G)
+            g = got[q_row0[b]:q_row0[b] + int(c.q_len[b]), h * G]
+            err = float(np.abs(g - ref).max())
+            cos = float(g.ravel() @ ref.ravel() / (np.linalg.norm(g) * np.linalg.norm(ref)))
+            print("%s complete head (request %d, query head %d, %s): %d rows maxabs=%.3e cos=%.8f"
+                  % (c.name, b, h * G, "GLOBAL" if kind == G_ else "LOCAL", len(g), err, cos),
+                  flush=True)
+            assert err <= MAXABS[c.dtype] and cos > COS_MIN
 
 
 def _random_cases(n=16, seed=2024):

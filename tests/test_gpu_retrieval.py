@@ -10,7 +10,8 @@ import torch
 import oracle
 from head_aware_paged_segpaged_amd import SegPagedLayer
 from head_aware_paged_segpaged_amd import binding as B
-from tests.helpers import COS_MIN, DEV, MAXABS, assert_parity, to_device, to_f64
+from tests.helpers import (COS_MIN, DEV, MAXABS, assert_parity, group_parity, to_device,
+                           to_f64)
 from workloads import (GLOBAL, LOCAL, RETRIEVAL, config_case, custom_case, free_list,
                        importance_scores)
 
@@ -111,9 +112,9 @@ def test_retrieval_table_decode_is_bitwise_the_planned_decode():
     assert torch.equal(a, b)
 
 
-def test_full_size_retrieval_workload_sampled():
+def test_full_size_retrieval_workload_all_rows():
     # The decode workload with two RETRIEVAL heads (10 % of each prefix kept): tables and
-    # kept lists bit-exact, two retrieval heads' pool rows bit-exact, sampled output rows
+    # kept lists bit-exact, two retrieval heads' pool rows bit-exact, every output row
     # against the oracle.
     c = config_case(7)
     imp = importance_scores(c)
@@ -141,15 +142,10 @@ def test_full_size_retrieval_workload_sampled():
         sl = torch.tensor([g[2] for g in got], dtype=torch.long, device=DEV)
         k = to_device(c.k, c.dtype)
         assert torch.equal(layer.k_pool[ph, sl], k[pos, h])
-    worst_abs, worst_cos = 0.0, 1.0
-    for _ in range(24):
-        b, hq = int(rng.integers(c.B)), int(rng.integers(c.Hq))
-        ref = oracle.attention_rows(c.q, c.k, c.v, c.ctx_len, c.q_len, c.policy, c.Hq, c.Hkv,
-                                    c.scale, c.dtype, b, hq, importance=imp)[0]
-        g = out[b, hq]
-        worst_abs = max(worst_abs, float(np.abs(g - ref).max()))
-        worst_cos = min(worst_cos, float(g @ ref / (np.linalg.norm(g) * np.linalg.norm(ref))))
-    print("%s sampled: maxabs=%.3e min_cos=%.8f" % (c.name, worst_abs, worst_cos), flush=True)
+    # every row: one decode query per (request, query head)
+    groups = [(b, h, np.array([0])) for b in range(c.B) for h in range(c.Hkv)]
+    worst_abs, worst_cos, rows = group_parity(c, out, groups, importance=imp, label="all rows")
+    assert rows == c.B * c.Hq
     assert worst_abs <= MAXABS[c.dtype] and worst_cos > COS_MIN
 
 
