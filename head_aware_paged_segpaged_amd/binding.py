@@ -54,6 +54,7 @@ EXPORTED = [
     "segpaged_attention_plan",
     "segpaged_attention",
     "segpaged_attention_profiled",
+    "segpaged_attention_static",
     "segpaged_attention_check",
     "segpaged_attention_plan_host",
     "segpaged_dense_mask_workspace_size",
@@ -110,6 +111,9 @@ _SIGS = {
     "segpaged_attention_profiled": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                                            _vp, _vp, _vp, _i64, _vp, _vp, _vp, _f, _vp, _vp,
                                            _sz, _vp, _vp, _vp]),
+    "segpaged_attention_static": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                         _vp, _vp, _vp, _i64, _vp, _vp, _vp, _f, _vp, _vp,
+                                         _vp]),
     "segpaged_attention_check": (_i32, [_vp, _sz, _vp]),
     "segpaged_attention_plan_host": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                             _vp, _i32, _i32, _vp, _sz, ctypes.POINTER(_sz),
@@ -422,6 +426,20 @@ def segpaged_attention_profiled(dtype, Hq: int, Hkv: int, D: int, page_size: int
     args += [_vp(main_begin.handle if main_begin else 0), _vp(main_end.handle if main_end else 0)]
     _check(lib().segpaged_attention_profiled(*args), "segpaged_attention_profiled")
     del keep
+
+
+def segpaged_attention_static(dtype, Hq: int, Hkv: int, D: int, page_size: int, ctx_len, q_len,
+                              policy, q, k_pool, v_pool, n_phys: int, seg_table, kv_len, v2p,
+                              scale: float, o, error=None, stream=None) -> None:
+    """segpaged_attention on the library's own device workspace (no workspace argument);
+    `error` is an optional device int32 tensor that receives the device-side status."""
+    c, ql, p = _host_i32(ctx_len), _host_i32(q_len), _host_i32(policy).reshape(-1, 3)
+    _check(lib().segpaged_attention_static(
+        _dtype_code(dtype), len(c), Hq, Hkv, D, page_size, _ptr(c), _ptr(ql), _ptr(p),
+        _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), int(n_phys),
+        _dev(seg_table, "seg_table"), _dev(kv_len, "kv_len"), _dev(v2p, "v2p"), float(scale),
+        _dev(o, "o"), _dev(error, "error") if error is not None else None, _stream(stream)),
+        "segpaged_attention_static")
 
 
 def segpaged_attention_check(workspace, stream=None) -> int:

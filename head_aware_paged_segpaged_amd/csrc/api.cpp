@@ -614,6 +614,53 @@ sp_status segpaged_attention(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
       nullptr, nullptr);
 }
 
+sp_status segpaged_attention_static(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                    int32_t D, int32_t page_size, const int32_t* ctx_len,
+                                    const int32_t* q_len, const sp_head_policy* pol,
+                                    const void* q, const void* k_pool, const void* v_pool,
+                                    int64_t n_phys, const int32_t* seg_table,
+                                    const int32_t* kv_len, const int32_t* v2p,
+                                    float softmax_scale, void* o, int32_t* error,
+                                    hipStream_t stream) {
+  const Shape s = make_shape(kModePaged, dtype, B, Hq, Hkv, D, page_size, ctx_len, q_len, pol);
+  sp_status st = check_shape(s);
+  if (st != SP_OK) return st;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return SP_ERR_INVALID_ARG;
+  bool need_pre = false, need_dec = false;
+  needed_kernels(s, &need_pre, &need_dec);
+  if (!need_pre && !need_dec) return SP_OK;
+  if (q == nullptr || k_pool == nullptr || v_pool == nullptr || o == nullptr ||
+      seg_table == nullptr || kv_len == nullptr || v2p == nullptr || n_phys < 1)
+    return SP_ERR_INVALID_ARG;
+  if (need_pre && s.P < kChunk &&
+      n_phys * int64_t(s.P) * s.D * (s.dtype == SP_BF16 ? 2 : 4) > int64_t(0x7fffffff))
+    return SP_ERR_UNSUPPORTED;
+  int32_t gp = 0, gd = 0;
+  st = grids(s, &gp, &gd);
+  if (st != SP_OK) return st;
+  Plan plan;
+  st = make_plan(s, gp, gd, &plan);
+  if (st != SP_OK) return st;
+  if (plan.bytes > kStaticWorkspaceBytes) return SP_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (static_workspace(&ws) != hipSuccess) return SP_ERR_HIP;
+  // The upload rewrites the header: the error word and the queue counters start at zero.
+  std::vector<uint8_t> buf;
+  serialize_plan(plan, &buf);
+  if (hipMemcpyAsync(ws, buf.data(), buf.size(), hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return SP_ERR_HIP;
+  combine_counts().put(plan.hdr.signature, plan.hdr.n_combine);
+  st = run_attention(s, q, k_pool, v_pool, n_phys, seg_table, kv_len, v2p, softmax_scale, o, ws,
+                     kStaticWorkspaceBytes, stream, nullptr, nullptr);
+  if (st != SP_OK) return st;
+  if (error != nullptr &&
+      hipMemcpyAsync(error, static_cast<uint8_t*>(ws) + kOffError, sizeof(int32_t),
+                     hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return SP_ERR_HIP;
+  return SP_OK;
+}
+
 sp_status segpaged_attention_profiled(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
                                       int32_t D, int32_t page_size, const int32_t* ctx_len,
                                       const int32_t* q_len, const sp_head_policy* pol,

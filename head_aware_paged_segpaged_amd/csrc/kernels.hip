@@ -22,6 +22,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "launch.h"
@@ -1572,6 +1573,33 @@ hipError_t launch_append(int32_t dtype, int32_t D, int grid, const AppendParams&
     else append_kernel<F32, 128><<<grid, 64, 0, stream>>>(p);
   }
   return hipGetLastError();
+}
+
+// Library-owned workspace for callers that cannot allocate device memory. Each GPU the library
+// runs on holds its own copy until the process ends. In host code `scratch` names a host-side
+// stand-in, not the device array: its device address comes from hipGetSymbolAddress, once per
+// device with that device current, and only that address is handed to kernels and copies.
+static __device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t static_workspace(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_build(int32_t dtype, int32_t D, const BuildParams& p, hipStream_t stream) {

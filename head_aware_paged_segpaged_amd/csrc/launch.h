@@ -63,6 +63,11 @@ struct AppendParams {
   int32_t pol[kMaxAppendHeads][3];  // (kind, sink, window) per KV head
 };
 
+// Bytes of the library-owned device workspace of segpaged_attention_static (one per GPU).
+constexpr size_t kStaticWorkspaceBytes = size_t(64) << 20;
+// Device address of that workspace on the current device (looked up once per device).
+hipError_t static_workspace(void** ptr);
+
 // Resident work groups per compute unit of the persistent attention kernels.
 int attention_occupancy(int32_t dtype, int32_t D, int32_t mode, bool decode);
 hipError_t launch_attention(int32_t dtype, int32_t D, int32_t mode, bool decode, int grid,

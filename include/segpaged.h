@@ -372,6 +372,27 @@ sp_status segpaged_attention(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
                              const int32_t* kv_len, const int32_t* v2p, float softmax_scale,
                              void* o, void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code that must not call hipMalloc, tight
+ * serving loops, harnesses that forbid allocation): segpaged_attention with no workspace
+ * argument. It plans on the host and uploads the plan (synchronising `stream`) into a
+ * library-owned device array of 64 MiB per GPU, held until the process ends, then runs the
+ * same kernels on it. It allocates no device memory. Plans larger than 64 MiB (many KV-split
+ * partial results) return SP_ERR_WORKSPACE_TOO_SMALL before anything is written. Every call on
+ * one GPU shares that GPU's array: calls that overlap in time on one GPU (any streams) race
+ * and give undefined results. Planning on every call is host work that segpaged_attention
+ * keeps out of the call (it plans once per layout).
+ *   error : device int32 or NULL; after the kernels, the call's device-side status (SP_OK,
+ *           SP_ERR_INVALID_ARG for a page id >= n_phys) is copied there on `stream`.
+ * Other arguments, errors and O: as segpaged_attention, bit for bit. */
+sp_status segpaged_attention_static(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                    int32_t D, int32_t page_size, const int32_t* ctx_len,
+                                    const int32_t* q_len, const sp_head_policy* pol,
+                                    const void* q, const void* k_pool, const void* v_pool,
+                                    int64_t n_phys, const int32_t* seg_table,
+                                    const int32_t* kv_len, const int32_t* v2p,
+                                    float softmax_scale, void* o, int32_t* error,
+                                    hipStream_t stream);
+
 /* Same as segpaged_attention, and records `main_begin` / `main_end` (may be NULL) on
  * `stream` right before and after the attention kernel(s), before any combine kernel, so a
  * caller can time the main kernel alone. */
