@@ -286,6 +286,33 @@ struct KVTile {
       }
     }
   }
+  // Full step of a pool whose pages hold at least one step: its 64 rows are contiguous
+  // (kBytes from `kb`). Wave w fills tile bytes [w * kWave, (w + 1) * kWave) with kLoads
+  // transfers that share one LDS base (M0) and one per-lane offset each: transfer j adds
+  // 1024 * j through the instruction's immediate offset, which the hardware adds to both the
+  // memory and the LDS address. `vo[j]` = memory offset of this lane's 16 bytes of transfer j,
+  // relative to the step's first row, minus 1024 * j (fast_voff).
+  static constexpr int kWave = kLoads * 1024;
+  static constexpr bool kFast = kLoads <= 4;  // immediate offsets up to 3072
+  __device__ __forceinline__ static uint32_t fast_voff(int j) {
+    const int byte = int(threadIdx.x >> 6) * kWave + 1024 * j + 16 * int(threadIdx.x & 63);
+    const int row = byte / kRowBytes, pc = (byte % kRowBytes) / 16;
+    return uint32_t(row * kRowBytes + swz(row, pc) * 16 - 1024 * j);
+  }
+  template <int J>
+  __device__ __forceinline__ static void dma_at(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t vo) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, vo, 0, 1024 * J, 0);
+  }
+  __device__ __forceinline__ static void dma_fast(const void* src, const uint32_t (&vo)[4],
+                                                  char* lds) {
+    static_assert(kFast, "fast transfers need kLoads <= 4");
+    const __amdgpu_buffer_rsrc_t r = rsrc(src);
+    char* dst = lds + uniform(int(threadIdx.x >> 6)) * kWave;
+    dma_at<0>(r, dst, vo[0]);
+    if constexpr (kLoads > 1) dma_at<1>(r, dst, vo[1]);
+    if constexpr (kLoads > 2) dma_at<2>(r, dst, vo[2]);
+    if constexpr (kLoads > 3) dma_at<3>(r, dst, vo[3]);
+  }
   // Pages smaller than a step: every row looks up its own page; offsets are taken from the
   // pool start (pools under 2 GiB, checked on the host).
   template <bool kK, bool kV>
@@ -432,6 +459,108 @@ __device__ __forceinline__ void issue_step(const AttnParams& p, const WorkItem& 
   }
 }
 
+// The KV steps of a prefill item, 64 at a time in one register per field: lane j describes
+// step win + j of the item. Read per step with v_readlane (no memory access, no wait), so the
+// step loop carries no page lookups or range arithmetic; refilled every 64 steps.
+//   lo, hi : paged, pages of at least one step: byte offset of the step's first row in the
+//            pool (64 bits); smaller pages: the step's first stored index and the segment's
+//            first virtual page; dense: byte offset of the step's first row in the dense K/V
+//   pos    : key position of slot 0
+//   rng    : valid slots vlo | vhi << 8; 0 for an empty step (past the item's end)
+struct StepLane {
+  uint32_t lo, hi;
+  int pos, rng;
+};
+constexpr int kFullRange = kChunk << 8;  // vlo 0, vhi 64
+
+template <int D, bool kDense, int RB>
+__device__ __forceinline__ StepLane fill_steps(const AttnParams& p, const WorkItem& w,
+                                               const ItemKV& kv, int n, int win) {
+  const int i = win + int(threadIdx.x & 63);
+  const int c = w.c_begin + i;
+  const bool ia = c < kv.n_ra;
+  const int lo = ia ? w.ra_begin : w.rb_begin;
+  const int hi = ia ? w.ra_end : w.rb_end;
+  const int base = ia ? w.ra_begin / kChunk + c : w.rb_begin / kChunk + (c - kv.n_ra);
+  const int seg = ia ? w.ra_seg : w.rb_seg;
+  const int ti0 = base * kChunk;
+  int vlo = max(0, lo - ti0), vhi = min(kChunk, hi - ti0);
+  if (i >= n || vhi <= vlo) vlo = vhi = 0;
+  StepLane s;
+  s.pos = kDense ? ti0 : (seg == 0 ? kv.pos0 : kv.pos1) + ti0;
+  uint64_t off = 0;
+  if constexpr (kDense) {
+    off = uint64_t((int64_t(w.kv_row0 + ti0) * p.Hkv + w.h) * RB);
+  } else {
+    const int vs = seg == 0 ? kv.vstart0 : kv.vstart1;
+    if (p.P >= kChunk) {
+      if (vhi > vlo) {
+        const int phys = p.v2p[vs + ti0 / p.P];
+        if (uint32_t(phys) >= uint64_t(p.n_phys)) {
+          set_error(p.ws, SP_ERR_INVALID_ARG);
+          vlo = vhi = 0;
+        } else {
+          off = uint64_t((int64_t(phys) * p.P + (ti0 & (p.P - 1))) * RB);
+        }
+      }
+    } else {
+      off = uint64_t(uint32_t(ti0)) | (uint64_t(uint32_t(vs)) << 32);
+    }
+  }
+  s.lo = uint32_t(off);
+  s.hi = uint32_t(off >> 32);
+  s.rng = vlo | (vhi << 8);
+  return s;
+}
+
+__device__ __forceinline__ StepLane read_step(const StepLane& t, int lane) {
+  StepLane s;
+  s.lo = uint32_t(__builtin_amdgcn_readlane(int(t.lo), lane));
+  s.hi = uint32_t(__builtin_amdgcn_readlane(int(t.hi), lane));
+  s.pos = __builtin_amdgcn_readlane(t.pos, lane);
+  s.rng = __builtin_amdgcn_readlane(t.rng, lane);
+  return s;
+}
+
+__device__ __forceinline__ StepLane no_step() { return StepLane{0u, 0u, 0, 0}; }
+
+__device__ __forceinline__ Step as_step(const StepLane& s) {
+  return Step{0, 0, s.rng & 0xff, s.rng >> 8, s.pos, 0};
+}
+
+// LDS-DMA of K (kK) or V of one step from its table entry. Full steps of a paged pool with
+// pages of at least one step take the fast transfers; partial steps (rows outside the valid
+// range read as zero), small pages and the dense path take the general ones; empty steps
+// issue nothing (their tile is never read).
+template <class E, int D, bool kDense, bool kK>
+__device__ __forceinline__ void issue_table_step(const AttnParams& p, const StepLane& s,
+                                                 const uint32_t (&vo)[4], char* lds) {
+  using T = KVTile<E, D>;
+  if (s.rng == 0) return;
+  const void* pool = kK ? p.k : p.v;
+  const uint64_t off = uint64_t(s.lo) | (uint64_t(s.hi) << 32);
+  const int vlo = s.rng & 0xff, vhi = s.rng >> 8;
+  if constexpr (!kDense && T::kFast) {
+    if (p.P >= kChunk && s.rng == kFullRange) {
+      T::dma_fast(static_cast<const char*>(pool) + off, vo, lds);
+      return;
+    }
+  }
+  if constexpr (kDense) {
+    const char* b = static_cast<const char*>(pool) + off;
+    T::template dma_strided<kK, !kK>(b, b, uint32_t(p.Hkv) * T::kRowBytes, vlo, vhi,
+                                     s.rng == kFullRange, lds, lds);
+  } else {
+    if (p.P >= kChunk) {
+      const char* b = static_cast<const char*>(pool) + off;
+      T::template dma_strided<kK, !kK>(b, b, T::kRowBytes, vlo, vhi, s.rng == kFullRange, lds,
+                                       lds);
+    } else {
+      T::template dma_small_pages<kK, !kK>(p, int(s.hi), int(s.lo), vlo, vhi, lds, lds);
+    }
+  }
+}
+
 template <class T>
 __device__ __forceinline__ T lds_ld(const char* p) {
   return *reinterpret_cast<const T*>(p);
@@ -568,6 +697,11 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
         vaddr[r][d] = T::off(8 * r + 4 * (g >> 1) + (s >> 2), 2 * (32 * d + 16 * (g & 1) + 4 * (s & 3)));
   }
 
+  // Per-lane memory offsets of the fast step transfers (shared by K and V).
+  uint32_t vo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) vo[j] = T::kFast && j < T::kLoads ? T::fast_voff(j) : 0u;
+
   for (;;) {
     if (tid == 0) s_item = pop_item(p.ws, hd->prefill_q, kOffPrefillCnt, xcd, exhausted, first);
     __syncthreads();
@@ -648,14 +782,18 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     // that happens on a row's first steps only, and the O rescale drops out of the loop.
     // Returns the reference the step's exponentials use.
     auto update_max = [&](const f32x16_t& a0, const f32x16_t& a1) -> float {
-      float m8[8];
+      // two chains of three-input maxima, then the other half-wave's value (rows of lane l
+      // and lane l ^ 32 are the same query row) through a half swap, no LDS round trip
+      float ma = fmaxf(fmaxf(a0[0], a0[1]), a0[2]), mb = fmaxf(fmaxf(a1[0], a1[1]), a1[2]);
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        m8[t] = fmaxf(fmaxf(a0[2 * t], a0[2 * t + 1]), fmaxf(a1[2 * t], a1[2 * t + 1]));
-#pragma unroll
-      for (int t = 0; t < 4; ++t) m8[t] = fmaxf(m8[t], m8[t + 4]);
-      float mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
+      for (int t = 3; t < 15; t += 2) {
+        ma = fmaxf(fmaxf(ma, a0[t]), a0[t + 1]);
+        mb = fmaxf(fmaxf(mb, a1[t]), a1[t + 1]);
+      }
+      ma = fmaxf(fmaxf(ma, a0[15]), fmaxf(mb, a1[15]));
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ma), __float_as_uint(ma),
+                                                       false, false);
+      float mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.scale_log2;
       if (__ballot(mx > m_run + kSlack) != 0) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = exp2_fast(m_run - (m_new == kNegInf ? 0.f : m_new));
@@ -673,12 +811,6 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
         a0[rr] = exp2_fast(__builtin_fmaf(a0[rr], p.scale_log2, -m_use));
         a1[rr] = exp2_fast(__builtin_fmaf(a1[rr], p.scale_log2, -m_use));
       }
-      float r8[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) r8[t] = (a0[2 * t] + a0[2 * t + 1]) + (a1[2 * t] + a1[2 * t + 1]);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) r8[t] += r8[t + 4];
-      l_run += (r8[0] + r8[1]) + (r8[2] + r8[3]);
       if constexpr (kBf16) {
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
@@ -687,7 +819,35 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
           pb[1][ii] = to_bf16x8(a1[8 * ii + 0], a1[8 * ii + 1], a1[8 * ii + 2], a1[8 * ii + 3],
                                 a1[8 * ii + 4], a1[8 * ii + 5], a1[8 * ii + 6], a1[8 * ii + 7]);
         }
+        // l += the row sums of the bf16 probabilities the P*V product uses, two per dot2.
+        // (The pairs are taken with shufflevector: taking them as bit casts of the vector's
+        // 32-bit words is folded wrongly by this compiler, into one word summed four times.)
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii) {
+            const bf16x8_t x = pb[kb][ii];
+            acc[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), ones,
+                                                     acc[0], false);
+            acc[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), ones,
+                                                     acc[1], false);
+            acc[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), ones,
+                                                     acc[2], false);
+            acc[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), ones,
+                                                     acc[3], false);
+          }
+        l_run += (acc[0] + acc[1]) + (acc[2] + acc[3]);
       } else {
+        float r8[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          r8[t] = (a0[2 * t] + a0[2 * t + 1]) + (a1[2 * t] + a1[2 * t + 1]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) r8[t] += r8[t + 4];
+        l_run += (r8[0] + r8[1]) + (r8[2] + r8[3]);
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) {
           pb[0][ii] = a0[ii];
@@ -735,47 +895,47 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     };
 
     const int n = w.c_end - w.c_begin;
-    auto step_at = [&](int i) {
-      return i < n ? describe_step<D, kDense>(p, w, kv, w.c_begin + i) : empty_step();
-    };
-    // Steps are described (page lookup included) one iteration before their first DMA.
-    Step prev = step_at(0);
-    Step cur = step_at(1);
-    Step nxt = step_at(2);
+    StepLane tab = fill_steps<D, kDense, RB>(p, w, kv, n, 0);
     // Prologue: S^T, mask and row maximum of step 0; K(1) and V(0) land meanwhile.
-    issue_step<E, D, kDense, true, false>(p, w, kv, prev, lk0, nullptr);
+    const StepLane s0 = read_step(tab, 0);
+    StepLane cur = n > 1 ? read_step(tab, 1) : no_step();  // step 1
+    issue_table_step<E, D, kDense, true>(p, s0, vo, lk0);
     kv_barrier<0>();
-    issue_step<E, D, kDense, true, false>(p, w, kv, cur, lk1, nullptr);
-    issue_step<E, D, kDense, false, true>(p, w, kv, prev, nullptr, lv0);
+    issue_table_step<E, D, kDense, true>(p, cur, vo, lk1);
+    issue_table_step<E, D, kDense, false>(p, s0, vo, lv0);
     f32x16_t sp0, sp1;
     qk(lk0, sp0, sp1);
-    mask(prev, sp0, sp1);
+    mask(as_step(s0), sp0, sp1);
     float mp = update_max(sp0, sp1);
     kv_barrier<0>();
 
     // Iteration i: S^T(i) on the matrix cores interleaved with the exponentials of step i-1,
     // then P*V(i-1) (one basic block, instruction mix set by step_schedule); then the mask and
     // row maximum of step i, and O and l move to the new reference if needed. K(i+1) and V(i)
-    // are in flight.
+    // are in flight. `cur` is step i; step i+1 comes from the step table (refilled when it
+    // starts a new window of 64).
     auto run_step = [&](auto stage_c, int i) {
       constexpr int stg = decltype(stage_c)::value;  // i & 1
-      issue_step<E, D, kDense, true, false>(p, w, kv, nxt, stg ? lk0 : lk1, nullptr);
-      issue_step<E, D, kDense, false, true>(p, w, kv, cur, nullptr, stg ? lv1 : lv0);
-      const Step nn = step_at(i + 2);
+      StepLane nxt = no_step();
+      if (i + 1 < n) {
+        if (((i + 1) & 63) == 0) tab = fill_steps<D, kDense, RB>(p, w, kv, n, i + 1);
+        nxt = read_step(tab, (i + 1) & 63);
+      }
+      issue_table_step<E, D, kDense, true>(p, nxt, vo, stg ? lk0 : lk1);
+      issue_table_step<E, D, kDense, false>(p, cur, vo, stg ? lv1 : lv0);
       f32x16_t sc0, sc1;
       qk(stg ? lk1 : lk0, sc0, sc1);
       F pb[2][16 / KPL];
       probs(sp0, sp1, mp, pb);
       pv(stg ? lv0 : lv1, pb);
-      if constexpr (kBf16)  // 32 scores per lane: 32 FMA + 16 packs, 32 exponentials, 32 adds
+      if constexpr (kBf16)  // 32 scores per lane: 32 FMA + 16 packs + 16 dot2, 32 exponentials
         step_schedule<2 * NQK, 48 / (2 * NQK), 32 / (2 * NQK), 4 * ND, 32 / (4 * ND), 4>();
-      mask(cur, sc0, sc1);
+      mask(as_step(cur), sc0, sc1);
       mp = update_max(sc0, sc1);
       kv_barrier<0>();
       sp0 = sc0;
       sp1 = sc1;
       cur = nxt;
-      nxt = nn;
     };
     for (int i = 1; i < n; i += 2) {
       run_step(std::integral_constant<int, 1>{}, i);
