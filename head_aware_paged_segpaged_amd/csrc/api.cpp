@@ -3,12 +3,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 #include <cmath>
 #include <cstring>
-#include <functional>
 #include <mutex>
-#include <thread>
 #include <vector>
 
 #include "launch.h"
@@ -26,6 +23,35 @@ sp_status device_cus(int* cus) {
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return SP_ERR_HIP;
   *cus = n > 0 ? n : 1;
+  return SP_OK;
+}
+
+// A stream of the library's own per device, with two events to fork it from a caller's stream
+// and join it back (RETRIEVAL selection runs there, beside the scatter). Default priority;
+// created on first use and kept until the process ends. `mu` orders the fork / join sequences
+// of concurrent calls.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+
+sp_status side_stream(SideStream** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static SideStream sides[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SP_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> g(mu);
+  SideStream& s = sides[dev];
+  if (s.stream == nullptr) {
+    if (hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess ||
+        hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess)
+      return SP_ERR_HIP;
+  }
+  *out = &s;
   return SP_OK;
 }
 
@@ -220,77 +246,31 @@ sp_status layout_impl(int32_t n_layers, int32_t B, const int32_t* ctx_len, const
   return make_layout_layers(n_layers, B, ctx_len, q_len, Hkv, pol, page_size, reserve, lay);
 }
 
-// Build of n_layers layers (growable when `reserve` is not null: single layer only).
-// Kept positions of every RETRIEVAL head of a single-layer layout, in (request, head) order:
-// the sink, then the top fraction of the other prefix tokens by importance (ties: lower
-// position), ascending. offsets[b * Hkv + h] = start of (b, h) in the list (-1: none). Heads
-// are independent and are shared out over host threads.
-sp_status retrieval_keep_lists(int32_t B, const int32_t* ctx_len, const int32_t* q_len,
-                               int32_t Hkv, const sp_head_policy* pol, const float* importance,
-                               std::vector<int32_t>* pos, std::vector<int64_t>* offsets) {
-  struct Task {
-    int64_t row0, out;
-    int32_t h, s, k, prefix;
-  };
-  std::vector<Task> tasks;
+// The kept lists of the RETRIEVAL heads of a single-layer layout, in (request, head) order:
+// per (request, head) with a non-empty list, one selection task (its sink, then the top
+// fraction of the other prefix tokens by importance, ascending; chosen on the device).
+// offsets[b * Hkv + h] = start of (b, h) in row_pos (-1: none); *total = entries of row_pos.
+void retrieval_tasks(int32_t B, const int32_t* ctx_len, const int32_t* q_len, int32_t Hkv,
+                     const sp_head_policy* pol, std::vector<SelectTask>* tasks,
+                     std::vector<int64_t>* offsets, int64_t* total) {
   offsets->assign(size_t(B) * Hkv, -1);
-  int64_t row0 = 0, total = 0;
+  int64_t row0 = 0, acc = 0;
   for (int32_t b = 0; b < B; ++b) {
     for (int32_t h = 0; h < Hkv; ++h) {
       if (pol[h].kind != SP_RETRIEVAL) continue;
       int32_t s = 0, k = 0;
       retrieval_counts(pol[h], ctx_len[b], q_len[b], &s, &k);
       if (s + k == 0) continue;
-      if (importance == nullptr) return SP_ERR_INVALID_ARG;
-      (*offsets)[size_t(b) * Hkv + h] = total;
-      tasks.push_back(Task{row0, total, h, s, k, ctx_len[b] - q_len[b]});
-      total += s + k;
+      (*offsets)[size_t(b) * Hkv + h] = acc;
+      tasks->push_back(SelectTask{int32_t(acc), int32_t(row0), h, s, k, ctx_len[b] - q_len[b] - s});
+      acc += s + k;
     }
     row0 += ctx_len[b];
   }
-  pos->assign(size_t(total), 0);
-  // longest heads first, so the threads finish together
-  std::stable_sort(tasks.begin(), tasks.end(),
-                   [](const Task& a, const Task& c) { return a.prefix > c.prefix; });
-  std::atomic<bool> bad{false};
-  std::atomic<size_t> next{0};
-  // Per head: the k-th largest importance t (a selection on a contiguous copy), then one pass
-  // in position order that takes every token above t and the lowest-positioned ones equal to
-  // t until k are taken, so the list comes out ascending.
-  auto work = [&]() {
-    std::vector<float> col, sel;
-    for (size_t t = next++; t < tasks.size(); t = next++) {
-      const Task& tk = tasks[t];
-      int32_t* out = pos->data() + tk.out;
-      for (int32_t j = 0; j < tk.s; ++j) out[j] = j;
-      const int32_t n = tk.prefix - tk.s;
-      col.resize(size_t(n));
-      for (int32_t j = 0; j < n; ++j) {
-        col[size_t(j)] = importance[(tk.row0 + tk.s + j) * Hkv + tk.h];
-        if (!std::isfinite(col[size_t(j)])) bad = true;
-      }
-      if (tk.k == 0) continue;
-      sel = col;
-      std::nth_element(sel.begin(), sel.begin() + (tk.k - 1), sel.end(), std::greater<float>());
-      const float thr = sel[size_t(tk.k - 1)];
-      int32_t above = 0;
-      for (float v : col) above += v > thr;
-      int32_t ties = tk.k - above, w = tk.s;
-      for (int32_t j = 0; j < n; ++j) {
-        const float v = col[size_t(j)];
-        if (v > thr || (v == thr && ties-- > 0)) out[w++] = tk.s + j;
-      }
-    }
-  };
-  const int n_threads = int(std::min<size_t>(
-      tasks.size(), size_t(std::max(1u, std::min(16u, std::thread::hardware_concurrency())))));
-  std::vector<std::thread> pool;
-  for (int i = 1; i < n_threads; ++i) pool.emplace_back(work);
-  work();
-  for (std::thread& th : pool) th.join();
-  return bad ? SP_ERR_INVALID_ARG : SP_OK;
+  *total = acc;
 }
 
+// Build of n_layers layers (growable when `reserve` is not null: single layer only).
 sp_status build_impl(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv, int32_t D,
                      int32_t page_size, const int32_t* ctx_len, const int32_t* q_len,
                      const int32_t* reserve, const sp_head_policy* pol, const void* k_dense,
@@ -309,15 +289,16 @@ sp_status build_impl(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv, i
   if (int64_t(n_layers) * t_total > 0x7fffffffLL) return SP_ERR_UNSUPPORTED;  // int32 rows
   if (B == 0) return SP_OK;
   if (seg_table == nullptr || kv_len == nullptr) return SP_ERR_INVALID_ARG;
-  std::vector<int32_t> keep;
+  std::vector<SelectTask> tasks;
   std::vector<int64_t> keep_off;
+  int64_t n_keep = 0;
   bool retrieval = false;
   for (size_t i = 0; i < size_t(n_layers) * Hkv; ++i) retrieval |= pol[i].kind == SP_RETRIEVAL;
   if (retrieval) {
     if (n_layers != 1) return SP_ERR_INVALID_ARG;
-    st = retrieval_keep_lists(B, ctx_len, q_len, Hkv, pol, importance, &keep, &keep_off);
-    if (st != SP_OK) return st;
-    if (!keep.empty() && row_pos == nullptr) return SP_ERR_INVALID_ARG;
+    retrieval_tasks(B, ctx_len, q_len, Hkv, pol, &tasks, &keep_off, &n_keep);
+    if (n_keep > 0 && (importance == nullptr || row_pos == nullptr)) return SP_ERR_INVALID_ARG;
+    if (n_keep > 0x7fffffffLL) return SP_ERR_UNSUPPORTED;
   }
   const int64_t n_virt = lay.n_virt;
   if (n_free < n_virt) return SP_ERR_POOL_TOO_SMALL;
@@ -334,7 +315,8 @@ sp_status build_impl(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv, i
   }
   // Tables: seg_table, kv_len and v2p. When the caller placed them back to back in one
   // allocation they go up in a single host-to-device copy (each copy from pageable memory
-  // costs tens of microseconds of fixed overhead), else in three.
+  // costs tens of microseconds of fixed overhead), else in three. A copy from pageable host
+  // memory returns once the source has been staged, so the host buffer may go out of scope.
   const size_t n_heads = size_t(n_layers) * B * Hkv;
   const size_t n_tab = n_heads * 8, n_kl = n_heads;
   const bool adjacent = kv_len == seg_table + n_tab && (n_virt == 0 || v2p == kv_len + n_kl);
@@ -355,12 +337,60 @@ sp_status build_impl(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv, i
                                      hipMemcpyHostToDevice, stream) != hipSuccess)
       return SP_ERR_HIP;
   }
-  if (!keep.empty() && hipMemcpyAsync(row_pos, keep.data(), keep.size() * 4,
-                                      hipMemcpyHostToDevice, stream) != hipSuccess)
-    return SP_ERR_HIP;
-  if (hipStreamSynchronize(stream) != hipSuccess) return SP_ERR_HIP;
+  // RETRIEVAL heads: the kept lists are chosen on the device by the selection kernel, on a
+  // side stream forked from `stream`, while the scatter copies every other segment; the kept
+  // prefixes are copied once the selection has joined back.
+  SideStream* side = nullptr;
+  if (!tasks.empty()) {
+    st = side_stream(&side);
+    if (st != SP_OK) return st;
+  }
+  std::unique_lock<std::mutex> side_lock;
+  if (side != nullptr) {
+    side_lock = std::unique_lock<std::mutex>(side->mu);
+    if (hipEventRecord(side->fork, stream) != hipSuccess ||
+        hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
+      return SP_ERR_HIP;
+    SelectParams sp_;
+    std::memset(&sp_, 0, sizeof(sp_));
+    sp_.imp = importance;
+    sp_.row_pos = row_pos;
+    sp_.Hkv = Hkv;
+    for (size_t t0 = 0; t0 < tasks.size(); t0 += kMaxSelectTasks) {
+      sp_.n_tasks = int32_t(std::min<size_t>(kMaxSelectTasks, tasks.size() - t0));
+      std::memcpy(sp_.t, tasks.data() + t0, size_t(sp_.n_tasks) * sizeof(SelectTask));
+      if (launch_select(sp_, side->stream) != hipSuccess) return SP_ERR_HIP;
+    }
+    if (hipEventRecord(side->join, side->stream) != hipSuccess) return SP_ERR_HIP;
+  }
 
-  // Scatter: one launch per run of at most kMaxBuildSegs non-empty segments, over all layers.
+  // Scatter: the chunks of each (layer, request) group are counted on the host; the groups'
+  // chunk offsets, first dense rows and (retrieval) kept-prefix offsets travel in the kernel
+  // arguments, so one launch covers as many groups as fit there (every workload here: all).
+  const int32_t n_groups_all = n_layers * B;
+  const bool gather = !keep_off.empty();
+  // per group: chunks of the segments copied straight (phase 0/1) and of the kept prefixes
+  std::vector<int32_t> g_plain(size_t(n_groups_all), 0), g_kept(size_t(n_groups_all), 0);
+  std::vector<int32_t> g_row0(size_t(n_groups_all), 0);
+  for (int32_t l = 0; l < n_layers; ++l) {
+    int64_t row0 = int64_t(l) * t_total;  // dense K/V of layer l start at row l * sum(ctx_len)
+    for (int32_t b = 0; b < B; ++b) {
+      const size_t g = size_t(l) * B + b;
+      int64_t plain = 0, kept = 0;
+      for (int32_t h = 0; h < Hkv; ++h) {
+        const HeadLayout& hl = lay.heads[g * Hkv + h];
+        const bool has_kept = gather && keep_off[size_t(b) * Hkv + h] >= 0;
+        for (int s_ = 0; s_ < hl.nseg; ++s_) {
+          const int64_t c = (hl.seg[s_].ntok + kChunk - 1) / kChunk;
+          (has_kept && s_ == 0 ? kept : plain) += c;
+        }
+      }
+      g_plain[g] = int32_t(plain);
+      g_kept[g] = int32_t(kept);
+      g_row0[g] = int32_t(row0);
+      row0 += ctx_len[b];
+    }
+  }
   BuildParams bp;
   std::memset(&bp, 0, sizeof(bp));
   bp.k = k_dense;
@@ -369,42 +399,51 @@ sp_status build_impl(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv, i
   bp.vp = v_pool;
   bp.v2p = v2p;
   bp.row_pos = row_pos;
+  bp.seg_table = seg_table;
   bp.Hkv = Hkv;
   bp.P = page_size;
-  auto flush = [&]() -> sp_status {
-    if (bp.nseg == 0) return SP_OK;
-    if (launch_build(dtype, D, bp, stream) != hipSuccess) return SP_ERR_HIP;
-    bp.nseg = 0;
-    bp.nchunks = 0;
-    return SP_OK;
-  };
-  for (int32_t l = 0; l < n_layers; ++l) {
-    int64_t row0 = int64_t(l) * t_total;  // dense K/V of layer l start at row l * sum(ctx_len)
-    for (int32_t b = 0; b < B; ++b) {
-      for (int32_t h = 0; h < Hkv; ++h) {
-        const HeadLayout& hl = lay.heads[(size_t(l) * B + b) * Hkv + h];
-        for (int s = 0; s < hl.nseg; ++s) {
-          const Segment& sg = hl.seg[s];
-          if (sg.ntok == 0) continue;
-          if (bp.nseg == kMaxBuildSegs) {
-            st = flush();
-            if (st != SP_OK) return st;
+  const int32_t per_group = 2 + (gather ? Hkv : 0);  // ints of kernel arguments per group
+  auto scatter = [&](int32_t phase, const std::vector<int32_t>& g_chunks) -> sp_status {
+    bp.phase = phase;
+    for (int32_t g0 = 0; g0 < n_groups_all;) {
+      int32_t n = 0;
+      int64_t total = 0;
+      while (g0 + n < n_groups_all && 1 + (n + 1) * per_group <= kBuildArgInts &&
+             total + g_chunks[size_t(g0 + n)] <= 0x7fffffffLL) {
+        total += g_chunks[size_t(g0 + n)];
+        ++n;
+      }
+      if (n == 0) return SP_ERR_UNSUPPORTED;  // one group's descriptors do not fit
+      bp.group0 = g0;
+      bp.n_groups = n;
+      int32_t* cb = bp.arr;
+      int32_t* r0 = bp.arr + n + 1;
+      int32_t* go = r0 + n;
+      int32_t acc = 0;
+      for (int32_t i = 0; i < n; ++i) {
+        cb[i] = acc;
+        acc += g_chunks[size_t(g0 + i)];
+        r0[i] = g_row0[size_t(g0 + i)];
+        if (gather) {
+          const int32_t b = (g0 + i) % B;  // retrieval builds have one layer
+          for (int32_t h = 0; h < Hkv; ++h) {
+            const int64_t o = keep_off[size_t(b) * Hkv + h];
+            go[size_t(i) * Hkv + h] = o < 0 ? -1 : int32_t(o);
           }
-          BuildSeg& e = bp.seg[bp.nseg++];
-          const bool gather = s == 0 && !keep_off.empty() && keep_off[size_t(b) * Hkv + h] >= 0;
-          e.chunk0 = bp.nchunks;
-          e.src_row0 = int32_t(row0 + (gather ? 0 : sg.pos));
-          e.vstart = sg.vstart;
-          e.ntok = sg.ntok;
-          e.h = h;
-          e.pos_off = gather ? int32_t(keep_off[size_t(b) * Hkv + h]) : -1;
-          bp.nchunks += (sg.ntok + kChunk - 1) / kChunk;
         }
       }
-      row0 += ctx_len[b];
+      cb[n] = acc;
+      if (acc > 0 && launch_build(dtype, D, bp, acc, stream) != hipSuccess) return SP_ERR_HIP;
+      g0 += n;
     }
-  }
-  return flush();
+    return SP_OK;
+  };
+  st = scatter(gather ? 1 : 0, g_plain);
+  if (st != SP_OK) return st;
+  if (side != nullptr && hipStreamWaitEvent(stream, side->join, 0) != hipSuccess)
+    return SP_ERR_HIP;
+  if (gather) return scatter(2, g_kept);
+  return SP_OK;
 }
 
 // Shape of a table-driven decode call: one query per request; ctx_hint only balances the

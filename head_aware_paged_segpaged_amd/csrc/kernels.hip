@@ -303,11 +303,12 @@ struct KVTile {
   __device__ __forceinline__ static void dma_at(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t vo) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, vo, 0, 1024 * J, 0);
   }
+  // `wb` = this wave's byte offset in the tile (wave * kWave, uniform).
   __device__ __forceinline__ static void dma_fast(const void* src, const uint32_t (&vo)[4],
-                                                  char* lds) {
+                                                  char* lds, int wb) {
     static_assert(kFast, "fast transfers need kLoads <= 4");
     const __amdgpu_buffer_rsrc_t r = rsrc(src);
-    char* dst = lds + uniform(int(threadIdx.x >> 6)) * kWave;
+    char* dst = lds + wb;
     dma_at<0>(r, dst, vo[0]);
     if constexpr (kLoads > 1) dma_at<1>(r, dst, vo[1]);
     if constexpr (kLoads > 2) dma_at<2>(r, dst, vo[2]);
@@ -473,9 +474,14 @@ struct StepLane {
 };
 constexpr int kFullRange = kChunk << 8;  // vlo 0, vhi 64
 
+// Bit of StepLane::rng: the step straddles a causal or window edge, or is not full, so its
+// scores need the visibility mask (the dense comparison path masks every step).
+constexpr int kNeedsMask = 1 << 16;
+
 template <int D, bool kDense, int RB>
 __device__ __forceinline__ StepLane fill_steps(const AttnParams& p, const WorkItem& w,
-                                               const ItemKV& kv, int n, int win) {
+                                               const ItemKV& kv, int n, int win, int kind,
+                                               int sink, int window, int pmin, int pmax) {
   const int i = win + int(threadIdx.x & 63);
   const int c = w.c_begin + i;
   const bool ia = c < kv.n_ra;
@@ -509,7 +515,10 @@ __device__ __forceinline__ StepLane fill_steps(const AttnParams& p, const WorkIt
   }
   s.lo = uint32_t(off);
   s.hi = uint32_t(off >> 32);
-  s.rng = vlo | (vhi << 8);
+  const int last = s.pos + kChunk - 1;
+  const bool clear = vlo == 0 && vhi == kChunk && last <= pmin &&
+                     (kind == SP_GLOBAL || last < sink || s.pos > pmax - window);
+  s.rng = vhi > vlo ? vlo | (vhi << 8) | (kDense || !clear ? kNeedsMask : 0) : 0;
   return s;
 }
 
@@ -525,7 +534,7 @@ __device__ __forceinline__ StepLane read_step(const StepLane& t, int lane) {
 __device__ __forceinline__ StepLane no_step() { return StepLane{0u, 0u, 0, 0}; }
 
 __device__ __forceinline__ Step as_step(const StepLane& s) {
-  return Step{0, 0, s.rng & 0xff, s.rng >> 8, s.pos, 0};
+  return Step{0, 0, s.rng & 0xff, (s.rng >> 8) & 0xff, s.pos, 0};
 }
 
 // LDS-DMA of K (kK) or V of one step from its table entry. Full steps of a paged pool with
@@ -534,27 +543,27 @@ __device__ __forceinline__ Step as_step(const StepLane& s) {
 // issue nothing (their tile is never read).
 template <class E, int D, bool kDense, bool kK>
 __device__ __forceinline__ void issue_table_step(const AttnParams& p, const StepLane& s,
-                                                 const uint32_t (&vo)[4], char* lds) {
+                                                 const uint32_t (&vo)[4], int wb, char* lds) {
   using T = KVTile<E, D>;
   if (s.rng == 0) return;
   const void* pool = kK ? p.k : p.v;
   const uint64_t off = uint64_t(s.lo) | (uint64_t(s.hi) << 32);
-  const int vlo = s.rng & 0xff, vhi = s.rng >> 8;
+  const int vlo = s.rng & 0xff, vhi = (s.rng >> 8) & 0xff;
+  const bool full = (s.rng & 0xffff) == kFullRange;
   if constexpr (!kDense && T::kFast) {
-    if (p.P >= kChunk && s.rng == kFullRange) {
-      T::dma_fast(static_cast<const char*>(pool) + off, vo, lds);
+    if (p.P >= kChunk && full) {
+      T::dma_fast(static_cast<const char*>(pool) + off, vo, lds, wb);
       return;
     }
   }
   if constexpr (kDense) {
     const char* b = static_cast<const char*>(pool) + off;
-    T::template dma_strided<kK, !kK>(b, b, uint32_t(p.Hkv) * T::kRowBytes, vlo, vhi,
-                                     s.rng == kFullRange, lds, lds);
+    T::template dma_strided<kK, !kK>(b, b, uint32_t(p.Hkv) * T::kRowBytes, vlo, vhi, full, lds,
+                                     lds);
   } else {
     if (p.P >= kChunk) {
       const char* b = static_cast<const char*>(pool) + off;
-      T::template dma_strided<kK, !kK>(b, b, T::kRowBytes, vlo, vhi, s.rng == kFullRange, lds,
-                                       lds);
+      T::template dma_strided<kK, !kK>(b, b, T::kRowBytes, vlo, vhi, full, lds, lds);
     } else {
       T::template dma_small_pages<kK, !kK>(p, int(s.hi), int(s.lo), vlo, vhi, lds, lds);
     }
@@ -697,7 +706,9 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
         vaddr[r][d] = T::off(8 * r + 4 * (g >> 1) + (s >> 2), 2 * (32 * d + 16 * (g & 1) + 4 * (s & 3)));
   }
 
-  // Per-lane memory offsets of the fast step transfers (shared by K and V).
+  // Per-lane memory offsets of the fast step transfers (shared by K and V), and this wave's
+  // byte offset in a tile.
+  const int wb = wave * T::kWave;
   uint32_t vo[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) vo[j] = T::kFast && j < T::kLoads ? T::fast_voff(j) : 0u;
@@ -759,12 +770,9 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
       }
     };
     // Masks step st where it straddles a causal or window edge or is not full.
-    auto mask = [&](const Step& st, f32x16_t& a0, f32x16_t& a1) {
-      const bool full = st.vlo == 0 && st.vhi == kChunk;
-      const int last = st.pos0 + kChunk - 1;
-      const bool clear = full && last <= pmin &&
-                         (kind == SP_GLOBAL || last < sink || st.pos0 > pmax - window);
-      if (kDense || !clear) {
+    auto mask = [&](const StepLane& sl, f32x16_t& a0, f32x16_t& a1) {
+      if (sl.rng & kNeedsMask) {
+        const Step st = as_step(sl);
         const bool dual = step_is_dual(st, kind, sink, window, pmin);
         const uint64_t mb = mask_bits(key_mask(st, p_row, kind, sink, window, dual, 4 * hh), dual);
         const uint32_t m_lo = uint32_t(mb), m_hi = uint32_t(mb >> 32);
@@ -895,17 +903,17 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     };
 
     const int n = w.c_end - w.c_begin;
-    StepLane tab = fill_steps<D, kDense, RB>(p, w, kv, n, 0);
+    StepLane tab = fill_steps<D, kDense, RB>(p, w, kv, n, 0, kind, sink, window, pmin, pmax);
     // Prologue: S^T, mask and row maximum of step 0; K(1) and V(0) land meanwhile.
     const StepLane s0 = read_step(tab, 0);
     StepLane cur = n > 1 ? read_step(tab, 1) : no_step();  // step 1
-    issue_table_step<E, D, kDense, true>(p, s0, vo, lk0);
+    issue_table_step<E, D, kDense, true>(p, s0, vo, wb, lk0);
     kv_barrier<0>();
-    issue_table_step<E, D, kDense, true>(p, cur, vo, lk1);
-    issue_table_step<E, D, kDense, false>(p, s0, vo, lv0);
+    issue_table_step<E, D, kDense, true>(p, cur, vo, wb, lk1);
+    issue_table_step<E, D, kDense, false>(p, s0, vo, wb, lv0);
     f32x16_t sp0, sp1;
     qk(lk0, sp0, sp1);
-    mask(as_step(s0), sp0, sp1);
+    mask(s0, sp0, sp1);
     float mp = update_max(sp0, sp1);
     kv_barrier<0>();
 
@@ -918,11 +926,12 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
       constexpr int stg = decltype(stage_c)::value;  // i & 1
       StepLane nxt = no_step();
       if (i + 1 < n) {
-        if (((i + 1) & 63) == 0) tab = fill_steps<D, kDense, RB>(p, w, kv, n, i + 1);
+        if (((i + 1) & 63) == 0) tab = fill_steps<D, kDense, RB>(p, w, kv, n, i + 1, kind, sink, window, pmin,
+                                         pmax);
         nxt = read_step(tab, (i + 1) & 63);
       }
-      issue_table_step<E, D, kDense, true>(p, nxt, vo, stg ? lk0 : lk1);
-      issue_table_step<E, D, kDense, false>(p, cur, vo, stg ? lv1 : lv0);
+      issue_table_step<E, D, kDense, true>(p, nxt, vo, wb, stg ? lk0 : lk1);
+      issue_table_step<E, D, kDense, false>(p, cur, vo, wb, stg ? lv1 : lv0);
       f32x16_t sc0, sc1;
       qk(stg ? lk1 : lk0, sc0, sc1);
       F pb[2][16 / KPL];
@@ -930,7 +939,7 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
       pv(stg ? lv0 : lv1, pb);
       if constexpr (kBf16)  // 32 scores per lane: 32 FMA + 16 packs + 16 dot2, 32 exponentials
         step_schedule<2 * NQK, 48 / (2 * NQK), 32 / (2 * NQK), 4 * ND, 32 / (4 * ND), 4>();
-      mask(as_step(cur), sc0, sc1);
+      mask(cur, sc0, sc1);
       mp = update_max(sc0, sc1);
       kv_barrier<0>();
       sp0 = sc0;
@@ -1443,10 +1452,16 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Build / scatter: one work group copies 64 stored tokens (K and V) of one segment from the
-// dense [T][Hkv][D] tensors into their pool pages (a RETRIEVAL head's kept-prefix segment takes
-// its tokens' positions from a list: a gather). Reads are whole D-rows, writes are whole
-// contiguous page rows; both are streaming (non-temporal) accesses, each byte is touched once.
+// Build / scatter: one launch copies every stored (token, head) row of every layer of the
+// batch from the dense [layer][T][Hkv][D] K/V into its pool page. A work group copies one
+// 64-token chunk of one segment. Chunks are numbered per (layer, request) group in (head,
+// segment) order; the group comes from a search of the per-group chunk offsets in the kernel
+// arguments, the head and segment from a wave-wide prefix sum over the group's rows of the
+// (already uploaded) seg_table. A RETRIEVAL head's kept-prefix segment takes its tokens'
+// positions from a list (a gather): layouts with such segments copy them in a launch of their
+// own (phase 2), after the selection that writes the list, and everything else before
+// (phase 1), so that the selection overlaps the bulk of the copy. Reads are whole D-rows,
+// writes whole contiguous page rows, both streaming (non-temporal): each byte is touched once.
 // ---------------------------------------------------------------------------------------
 template <class E, int D>
 __global__ void __launch_bounds__(256) build_kernel(BuildParams p) {
@@ -1455,14 +1470,62 @@ __global__ void __launch_bounds__(256) build_kernel(BuildParams p) {
   constexpr int kCols = D / kVec;
   constexpr int kLoads = kChunk * kCols / 256;
   const int c = blockIdx.x;
-  // Segment of this unit: last entry with chunk0 <= c (kernel arguments, uniform).
-  int lo = 0, hi = p.nseg - 1;
+  const int32_t* cb = p.arr;                     // chunk offsets of the groups [n_groups + 1]
+  const int32_t* row0 = p.arr + p.n_groups + 1;  // first dense row of each group [n_groups]
+  const int32_t* gofs = row0 + p.n_groups;       // gather offsets [n_groups][Hkv] (retrieval)
+  // group: last g with cb[g] <= c (kernel arguments, uniform)
+  int lo = 0, hi = p.n_groups - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (p.seg[mid].chunk0 <= c) lo = mid; else hi = mid - 1;
+    if (cb[mid] <= c) lo = mid; else hi = mid - 1;
   }
-  const BuildSeg sg = p.seg[lo];
-  const int ti0 = (c - sg.chunk0) * kChunk;
+  const int g = lo, lc = c - cb[g];
+  // Head and segment of the group's chunk lc: lanes take heads lane and lane + 64, count
+  // their chunks (segment 0, then 1), and a prefix sum over the lanes orders them.
+  const int lane = __lane_id();
+  const int32_t* rows = p.seg_table + int64_t(p.group0 + g) * p.Hkv * 8;
+  int h = -1, s = 0, chunk = 0, base = 0;
+  for (int half = 0; half < 2 && h < 0; ++half) {
+    const int hh = lane + 64 * half;
+    int n0 = 0, n1 = 0;
+    if (hh < p.Hkv) {
+      n0 = (rows[hh * 8 + 1] + kChunk - 1) / kChunk;
+      n1 = (rows[hh * 8 + 5] + kChunk - 1) / kChunk;
+      if (p.phase != 0) {  // segment 0 of a head with a kept prefix is its gather segment
+        const bool kept = gofs[g * p.Hkv + hh] >= 0;
+        if (p.phase == 1 && kept) n0 = 0;
+        if (p.phase == 2) {
+          n0 = kept ? n0 : 0;
+          n1 = 0;
+        }
+      }
+    }
+    int incl = n0 + n1;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    const int excl = base + incl - (n0 + n1);
+    const uint64_t hit = __ballot(lc >= excl && lc < base + incl);
+    if (hit != 0) {
+      const int l = int(__builtin_ctzll(hit));
+      const int e = __shfl(excl, l), m0 = __shfl(n0, l);
+      h = l + 64 * half;
+      s = lc - e < m0 ? 0 : 1;
+      chunk = lc - e - (s ? m0 : 0);
+    }
+    base += __shfl(incl, 63);
+  }
+  h = uniform(h);
+  if (h < 0) return;  // past the group's chunks (never for a launch the host sized)
+  s = uniform(s);
+  chunk = uniform(chunk);
+  const int32_t* sr = rows + h * 8 + 4 * s;
+  const int pos = uniform(sr[0]), ntok = uniform(sr[1]), vstart = uniform(sr[2]);
+  const int pos_off = p.phase == 2 ? uniform(gofs[g * p.Hkv + h]) : -1;
+  const int src_row0 = row0[g] + (pos_off < 0 ? pos : 0);
+  const int ti0 = chunk * kChunk;
   const int lp = __builtin_ctz(unsigned(p.P));  // page size: a power of two
   const S* kd = static_cast<const S*>(p.k);
   const S* vd = static_cast<const S*>(p.v);
@@ -1477,18 +1540,162 @@ __global__ void __launch_bounds__(256) build_kernel(BuildParams p) {
   for (int j = 0; j < kLoads; ++j) {
     const int idx = threadIdx.x + 256 * j;
     const int row = idx / kCols, col = idx % kCols;
-    const int ti = min(ti0 + row, sg.ntok - 1);
-    const int tok = sg.pos_off < 0 ? ti : p.row_pos[sg.pos_off + ti];
-    const int64_t src = (int64_t(sg.src_row0 + tok) * p.Hkv + sg.h) * D + col * kVec;
+    const int ti = min(ti0 + row, ntok - 1);
+    const int tok = pos_off < 0 ? ti : p.row_pos[pos_off + ti];
+    const int64_t src = (int64_t(src_row0 + tok) * p.Hkv + h) * D + col * kVec;
     kr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kd + src));
     vr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vd + src));
-    const int phys = p.v2p[sg.vstart + (ti >> lp)];
+    const int phys = p.v2p[vstart + (ti >> lp)];
     dst[j] = ((int64_t(phys) << lp) + (ti & (p.P - 1))) * D + col * kVec;
   }
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) {
     __builtin_nontemporal_store(kr[j], reinterpret_cast<u32x4_t*>(kp + dst[j]));
     __builtin_nontemporal_store(vr[j], reinterpret_cast<u32x4_t*>(vp + dst[j]));
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// RETRIEVAL selection (page "RedKnot head classification", the four head types: a retrieval
+// head keeps only the top fraction of tokens by importance). One work group per (request,
+// retrieval head) task writes the head's kept positions ascending: its sink, then the k most
+// important of the other n prefix tokens, ties going to the lower position. Importance values
+// map to unsigned keys in the same order; the k-th largest key T comes from a radix select
+// over three digits (12, 12 and 8 bits, one histogram pass each), then one pass in position
+// order takes every key above T and the first (k - count above T) keys equal to T.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(x, d);
+    if (lane >= d) x += t;
+  }
+  return x;
+}
+
+constexpr int kSelectThreads = 1024;
+
+__global__ void __launch_bounds__(kSelectThreads) select_kernel(SelectParams p) {
+  // Histogram words in LDS: passes of 10, 11 and 11 key bits, each histogram held in several
+  // copies (lane l adds to copy l % copies) so that lanes of one wave whose keys share a bin
+  // rarely hit the same word: importance values crowd into few bins of the top bits.
+  constexpr int kWords = 16384;
+  constexpr int kWaves = kSelectThreads / 64;
+  constexpr int kBatch = 8;  // keys per thread in flight in the histogram passes
+  __shared__ uint32_t hist[kWords];
+  __shared__ int s_pick[2];
+  __shared__ int s_wave[kWaves];
+  const SelectTask t = p.t[blockIdx.x];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* out = p.row_pos + t.out;
+  for (int i = tid; i < t.sink; i += kSelectThreads) out[i] = i;
+  if (t.k <= 0) return;
+  const float* col = p.imp + (int64_t(t.row0) + t.sink) * p.Hkv + t.h;  // candidate j: col[j * Hkv]
+  uint32_t prefix = 0, pmask = 0;
+  int remaining = t.k;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int bits = pass == 0 ? 10 : 11;
+    const int shift = pass == 0 ? 22 : pass == 1 ? 11 : 0;
+    const int nb = 1 << bits, copies = kWords >> bits;
+    uint32_t* mine = hist + (lane & (copies - 1)) * nb;
+    for (int i = tid; i < kWords; i += kSelectThreads) hist[i] = 0;
+    __syncthreads();
+    for (int j0 = 0; j0 < t.n; j0 += kSelectThreads * kBatch) {
+      uint32_t key[kBatch];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        const int j = j0 + e * kSelectThreads + tid;
+        key[e] = j < t.n ? order_key(col[int64_t(j) * p.Hkv]) : 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        const int j = j0 + e * kSelectThreads + tid;
+        if (j < t.n && (key[e] & pmask) == prefix)
+          atomicAdd(&mine[(key[e] >> shift) & uint32_t(nb - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    for (int b = tid; b < nb; b += kSelectThreads) {  // fold the copies into copy 0
+      uint32_t sum = hist[b];
+      for (int c = 1; c < copies; ++c) sum += hist[c * nb + b];
+      hist[b] = sum;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l sums its run of bins, taken from the top: nb-1-per*l down to nb-per*(l+1)
+      const int per = nb / 64;
+      int sum = 0;
+      for (int i = 0; i < per; ++i) sum += int(hist[nb - 1 - per * lane - i]);
+      const int incl = wave_incl_sum(sum);  // keys in the top runs, through this lane's
+      const uint64_t hit = __ballot(incl >= remaining && incl - sum < remaining);
+      const int l = hit ? int(__builtin_ctzll(hit)) : 63;
+      if (lane == l) {
+        int above = incl - sum, d = nb - 1 - per * l;
+        for (int i = 0; i < per - 1; ++i, --d) {
+          const int c = int(hist[d]);
+          if (above + c >= remaining) break;
+          above += c;
+        }
+        s_pick[0] = d;
+        s_pick[1] = remaining - above;
+      }
+    }
+    __syncthreads();
+    prefix |= uint32_t(s_pick[0]) << shift;
+    pmask |= uint32_t(nb - 1) << shift;
+    remaining = s_pick[1];
+    __syncthreads();
+  }
+  // prefix = T, the k-th largest key; `remaining` keys equal to T are taken (the lowest).
+  const uint32_t T = prefix;
+  const int ties = remaining;
+  constexpr int kPer = 8;  // consecutive candidates per thread and tile
+  int gt_base = 0, eq_base = 0;
+  for (int j0 = 0; j0 < t.n; j0 += kSelectThreads * kPer) {
+    uint32_t gt = 0, eq = 0;  // bit e: candidate j0 + kPer * tid + e
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int j = j0 + kPer * tid + e;
+      if (j < t.n) {
+        const uint32_t key = order_key(col[int64_t(j) * p.Hkv]);
+        gt |= uint32_t(key > T) << e;
+        eq |= uint32_t(key == T) << e;
+      }
+    }
+    // prefix counts of (above, equal) over the threads of the tile, packed in one int (each
+    // count is at most kSelectThreads * kPer < 2^16)
+    const int mine = (__builtin_popcount(gt) << 16) | __builtin_popcount(eq);
+    const int incl = wave_incl_sum(mine);
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int before = incl - mine, tot = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const int x = s_wave[w];
+      before += w < wave ? x : 0;
+      tot += x;
+    }
+    __syncthreads();
+    int g_before = gt_base + (before >> 16), e_before = eq_base + (before & 0xffff);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const bool is_gt = (gt >> e) & 1, is_eq = (eq >> e) & 1;
+      if (is_gt || (is_eq && e_before < ties)) {
+        const int slot = g_before + min(e_before, ties);
+        out[t.sink + slot] = t.sink + j0 + kPer * tid + e;
+      }
+      g_before += is_gt;
+      e_before += is_eq;
+    }
+    gt_base += tot >> 16;
+    eq_base += tot & 0xffff;
   }
 }
 
@@ -1762,15 +1969,22 @@ hipError_t static_workspace(void** ptr) {
   return hipSuccess;
 }
 
-hipError_t launch_build(int32_t dtype, int32_t D, const BuildParams& p, hipStream_t stream) {
-  if (p.nchunks <= 0) return hipSuccess;
+hipError_t launch_build(int32_t dtype, int32_t D, const BuildParams& p, int n_chunks,
+                        hipStream_t stream) {
+  if (n_chunks <= 0) return hipSuccess;
   if (dtype == SP_BF16) {
-    if (D == 64) build_kernel<BF16, 64><<<p.nchunks, 256, 0, stream>>>(p);
-    else build_kernel<BF16, 128><<<p.nchunks, 256, 0, stream>>>(p);
+    if (D == 64) build_kernel<BF16, 64><<<n_chunks, 256, 0, stream>>>(p);
+    else build_kernel<BF16, 128><<<n_chunks, 256, 0, stream>>>(p);
   } else {
-    if (D == 64) build_kernel<F32, 64><<<p.nchunks, 256, 0, stream>>>(p);
-    else build_kernel<F32, 128><<<p.nchunks, 256, 0, stream>>>(p);
+    if (D == 64) build_kernel<F32, 64><<<n_chunks, 256, 0, stream>>>(p);
+    else build_kernel<F32, 128><<<n_chunks, 256, 0, stream>>>(p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
+  if (p.n_tasks <= 0) return hipSuccess;
+  select_kernel<<<p.n_tasks, kSelectThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 

@@ -24,27 +24,45 @@ struct AttnParams {
   float scale_log2;  // softmax_scale * log2(e)
 };
 
-struct BuildSeg {
-  int32_t chunk0;    // first 64-token copy unit of this segment in the launch
-  int32_t src_row0;  // dense row of the segment's first stored token (gather: of position 0)
-  int32_t vstart;    // first virtual page of the segment
-  int32_t ntok;
-  int32_t h;
-  int32_t pos_off;  // -1: tokens are consecutive; else token i is at position row_pos[pos_off + i]
-};
-
-constexpr int kMaxBuildSegs = 128;
+// Build: the kernel arguments carry, for each (layer, request) group of one launch, its first
+// chunk (64 stored tokens of one segment) among the launch's chunks, the dense row of the
+// group's first token and, for RETRIEVAL layouts, the kept-list offset of each head's kept
+// segment (-1: none). Heads and segments come from the uploaded seg_table.
+constexpr int kBuildArgInts = 944;
 
 struct BuildParams {
-  const void* k;
+  const void* k;  // dense [n_layers][T][Hkv][D]
   const void* v;
-  void* kp;
+  void* kp;  // pools [n_phys][P][D]
   void* vp;
   const int32_t* v2p;
-  const int32_t* row_pos;  // kept positions of RETRIEVAL segments (gather segments only)
-  int32_t Hkv, P, nseg, nchunks;
-  BuildSeg seg[kMaxBuildSegs];
+  const int32_t* row_pos;    // kept positions of RETRIEVAL segments (gather layouts only)
+  const int32_t* seg_table;  // device [n_layers][B][Hkv][2][4], uploaded before the launch
+  int32_t Hkv, P, n_groups, group0;
+  // 0: every segment; 1: every segment but the kept prefixes of RETRIEVAL heads (their
+  // positions are still being chosen); 2: only those kept prefixes (a gather through row_pos)
+  int32_t phase, pad;
+  // chunk offsets [n_groups + 1], first dense rows [n_groups], gather offsets [n_groups][Hkv]
+  // (phases 1 and 2: -1 for heads without a kept prefix)
+  int32_t arr[kBuildArgInts];
 };
+static_assert(sizeof(BuildParams) <= 4000, "build arguments fit the kernel argument segment");
+
+// RETRIEVAL selection: one task per (request, retrieval head) with a non-empty kept list.
+struct SelectTask {
+  int32_t out;   // first entry of the task's kept list in row_pos
+  int32_t row0;  // dense row of the request's position 0
+  int32_t h, sink, k, n;  // KV head, sink tokens, kept candidates, candidates (sink .. prefix-1)
+};
+constexpr int kMaxSelectTasks = 160;
+
+struct SelectParams {
+  const float* imp;  // device [T][Hkv]
+  int32_t* row_pos;
+  int32_t Hkv, n_tasks;
+  SelectTask t[kMaxSelectTasks];
+};
+static_assert(sizeof(SelectParams) <= 4000, "selection arguments fit the kernel argument segment");
 
 constexpr int kMaxAppendHeads = 128;
 
@@ -74,7 +92,9 @@ hipError_t launch_attention(int32_t dtype, int32_t D, int32_t mode, bool decode,
                             const AttnParams& p, hipStream_t stream);
 hipError_t launch_combine(int32_t dtype, int32_t D, int grid, const AttnParams& p,
                           hipStream_t stream);
-hipError_t launch_build(int32_t dtype, int32_t D, const BuildParams& p, hipStream_t stream);
+hipError_t launch_build(int32_t dtype, int32_t D, const BuildParams& p, int n_chunks,
+                        hipStream_t stream);
+hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 hipError_t launch_append(int32_t dtype, int32_t D, int grid, const AppendParams& p,
                          hipStream_t stream);
 

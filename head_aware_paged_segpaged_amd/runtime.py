@@ -17,6 +17,13 @@ from . import binding as B
 _TORCH = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
+def _device_f32(x, device) -> torch.Tensor:
+    """A contiguous float32 device tensor holding x (a tensor or a host array)."""
+    if isinstance(x, torch.Tensor):
+        return x.to(device=device, dtype=torch.float32).contiguous()
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.float32))).to(device)
+
+
 def _dt(dtype) -> str:
     return "bf16" if B._dtype_code(dtype) == B.SP_BF16 else "f32"
 
@@ -41,7 +48,8 @@ class SegPagedLayer:
     def build(self, k_dense: torch.Tensor, v_dense: torch.Tensor, free_pages,
               n_phys: int | None = None, stream=None, importance=None) -> None:
         """Allocate the pool and tables and fill them from dense [T, Hkv, D] K/V. Layouts with
-        RETRIEVAL heads need ``importance`` (host float32 [T, Hkv])."""
+        RETRIEVAL heads need ``importance`` (float32 [T, Hkv], a device tensor or host array,
+        kept on the device for rebuilds)."""
         fl = np.asarray(free_pages, dtype=np.int32)
         self.n_phys = int(n_phys if n_phys is not None else max(self.n_virt, 1))
         t = _TORCH[self.dtype]
@@ -57,7 +65,7 @@ class SegPagedLayer:
         self.kv_len = tables[n_tab:n_tab + n_kl].view(Bn, self.Hkv)
         self.v2p = tables[n_tab + n_kl:]
         if importance is not None:
-            self.importance = np.ascontiguousarray(np.asarray(importance, dtype=np.float32))
+            self.importance = _device_f32(importance, self.device)
             n_rows = B.segpaged_retrieval_rows(self.ctx_len, self.q_len, self.policy)
             self.row_pos = torch.zeros((max(n_rows, 1),), dtype=torch.int32, device=self.device)
         self.rebuild(k_dense, v_dense, fl, stream)
@@ -201,7 +209,8 @@ class SegPagedDecoder:
 
     def build(self, k_dense: torch.Tensor, v_dense: torch.Tensor, free_pages,
               n_phys: int | None = None, stream=None, importance=None) -> None:
-        """Layouts with RETRIEVAL heads need ``importance`` (host float32 [T, Hkv])."""
+        """Layouts with RETRIEVAL heads need ``importance`` (float32 [T, Hkv], a device tensor
+        or host array)."""
         self.n_phys = int(n_phys if n_phys is not None else max(self.n_virt, 1))
         t = _TORCH[self.dtype]
         self.k_pool = torch.empty((max(self.n_phys, 1), self.P, self.D), dtype=t,
@@ -220,7 +229,8 @@ class SegPagedDecoder:
             n_rows = B.segpaged_retrieval_rows(self.ctx_len, self.q_len, self.policy)
             self.row_pos = torch.zeros((max(n_rows, 1),), dtype=torch.int32, device=self.device)
             B.segpaged_build_scored(self.dtype, self.D, self.P, self.ctx_len, self.q_len,
-                                    self.policy, importance, k_dense, v_dense, fl, self.n_phys,
+                                    self.policy, _device_f32(importance, self.device), k_dense,
+                                    v_dense, fl, self.n_phys,
                                     self.k_pool, self.v_pool, self.seg_table, self.kv_len,
                                     self.v2p, self.row_pos, stream, reserve=self.reserve)
         else:

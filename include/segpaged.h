@@ -151,10 +151,14 @@ sp_status segpaged_layout_tables(int32_t B, const int32_t* ctx_len, const int32_
  *   seg_table        : device int32 [B][Hkv][2][4]   (written)
  *   kv_len           : device int32 [B][Hkv]         (written)
  *   v2p              : device int32 [n_virt]         (written; n_virt = segpaged_plan_pages)
- * The tables are uploaded with a copy that completes before return (one copy when kv_len
- * directly follows seg_table and v2p directly follows kv_len in memory, else three); the
- * scatter kernel runs asynchronously on `stream`. Errors: SP_ERR_POOL_TOO_SMALL if n_free < n_virt,
- * SP_ERR_INVALID_ARG for duplicate or out-of-range free-list entries. */
+ * The tables go up in one host-to-device copy on `stream` when kv_len directly follows
+ * seg_table and v2p directly follows kv_len in memory (else three); host arrays are read
+ * before return. Then one scatter launch (a work group per 64 stored tokens of a segment,
+ * finding its segment from the uploaded seg_table) copies every stored row; it runs
+ * asynchronously on `stream`. Batches with more (layer, request) groups than one launch's
+ * arguments hold (about 470, or 940 / (Hkv + 2) with RETRIEVAL heads) take one launch per
+ * such run of groups. Errors: SP_ERR_POOL_TOO_SMALL if n_free < n_virt, SP_ERR_INVALID_ARG
+ * for duplicate or out-of-range free-list entries. */
 sp_status segpaged_build(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int32_t page_size,
                          const int32_t* ctx_len, const int32_t* q_len, const sp_head_policy* pol,
                          const void* k_dense, const void* v_dense,
@@ -242,9 +246,14 @@ sp_status segpaged_retrieval_rows(int32_t B, const int32_t* ctx_len, const int32
  * plus:
  *   reserve    : host int32 [B] or NULL: with it the layout is the growable one of
  *                segpaged_build_growable (below), RETRIEVAL heads included
- *   importance : host float [sum(ctx_len)][Hkv], token-major like k_dense; only the prefix
- *                tokens of RETRIEVAL heads are read; a non-finite value there is
- *                SP_ERR_INVALID_ARG.
+ *   importance : device float [sum(ctx_len)][Hkv], token-major like k_dense; only the prefix
+ *                tokens of RETRIEVAL heads are read, on the device, by one selection work
+ *                group per (request, retrieval head). The selection runs on a stream of the
+ *                library's own (one per device, default priority, created on first use), forked
+ *                from `stream` after the table upload and joined back before the kept
+ *                prefixes are copied, so it overlaps the copy of every other segment; the call
+ *                stays ordered on `stream` like segpaged_build. Values must be finite (a NaN
+ *                orders by its bits: a valid but unspecified selection).
  *   row_pos    : device int32 [segpaged_retrieval_rows] (written): the kept positions of each
  *                RETRIEVAL head, ascending, heads in (request, head) order; may be NULL when
  *                that count is 0.

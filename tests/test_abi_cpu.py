@@ -255,16 +255,17 @@ def test_retrieval_layout_tables_and_invalid_arguments():
     lib = binding.lib()
     fake = binding._vp(256)
     c, ql, p = (np.array(x, np.int32) for x in ([100], [1], pol))
-    # the plain build has no importance for the kept rows; the scored build rejects NaN
+    # the plain build has no importance for the kept rows; the scored build needs importance
+    # (device) and row_pos when some head keeps rows, and checks that before queuing anything
     assert lib.segpaged_build(0, 1, 1, 128, 64, binding._ptr(c), binding._ptr(ql),
                               binding._ptr(p), fake, fake, binding._ptr(np.arange(4, dtype=np.int32)),
                               4, 4, fake, fake, fake, fake, fake, None) == E.SP_ERR_INVALID_ARG
-    imp = np.ones((100, 1), np.float32)
-    imp[50, 0] = np.nan
-    assert lib.segpaged_build_scored(0, 1, 1, 128, 64, binding._ptr(c), binding._ptr(ql), None,
-                                     binding._ptr(p), binding._ptr(imp), fake, fake,
-                                     binding._ptr(np.arange(4, dtype=np.int32)), 4, 4, fake,
-                                     fake, fake, fake, fake, fake, None) == E.SP_ERR_INVALID_ARG
+    for imp, rp in ((None, fake), (fake, None)):
+        assert lib.segpaged_build_scored(0, 1, 1, 128, 64, binding._ptr(c), binding._ptr(ql),
+                                         None, binding._ptr(p), imp, fake, fake,
+                                         binding._ptr(np.arange(4, dtype=np.int32)), 4, 4, fake,
+                                         fake, fake, fake, fake, rp, None) == \
+            E.SP_ERR_INVALID_ARG
 
 
 def test_layers_build_rejects_retrieval_heads():

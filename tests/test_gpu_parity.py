@@ -372,3 +372,40 @@ def test_layers_share_one_pool():
         torch.cuda.synchronize()
         assert m.check(layer) == 0
         assert_parity(to_f64(out), _oracle(c), c, "layer %d" % layer)
+
+
+@pytest.mark.parametrize("P", [16, 64, 256])
+def test_build_many_segments_and_groups(P):
+    # One build call over several layers with hundreds of segments (one scatter launch), and
+    # one over 520 requests (more (layer, request) groups than one launch's arguments hold, so
+    # the groups take two launches): tables equal the oracle's and every stored row of every
+    # layer equals its dense row bit for bit.
+    from head_aware_paged_segpaged_amd import SegPagedLayers
+    rng = np.random.default_rng(900 + P)
+    for n_layers, B, Hkv, lo, hi in ((5, 6, 8, 1, 3000), (1, 520, 2, 1, 200)):
+        ctx = rng.integers(lo, hi, B)
+        q = np.minimum(ctx, rng.choice([1, 7, 64, 300], B))
+        policies = [[(G_, 0, 1) if rng.random() < 0.3 else
+                     (L_, int(rng.choice([0, 4, 70])), int(rng.choice([1, 33, 200, 900])))
+                     for _ in range(Hkv)] for _ in range(n_layers)]
+        cases = [custom_case(1000 + 10 * P + i, dtype="bf16", Hq=Hkv, Hkv=Hkv, D=64, P=P,
+                             ctx_len=list(ctx), q_len=list(q), policy=pol)
+                 for i, pol in enumerate(policies)]
+        c0 = cases[0]
+        seg_o, kvl_o, n_virt = oracle.plan_tables_layers(c0.ctx_len, c0.q_len, policies, P)
+        n_segs = int((seg_o[..., 1] > 0).sum())
+        print("case build layers %d requests %d heads %d P %d: %d segments"
+              % (n_layers, B, Hkv, P, n_segs), flush=True)
+        assert n_segs > 128
+        m = SegPagedLayers(c0.dtype, n_layers, c0.Hq, c0.Hkv, c0.D, P, c0.ctx_len, c0.q_len,
+                           policies, DEV)
+        stack = lambda xs: torch.stack([to_device(x, c0.dtype) for x in xs])
+        n_phys = m.n_virt + 3
+        fl = np.random.default_rng(P).permutation(n_phys).astype(np.int32)
+        m.build(stack([c.k for c in cases]), stack([c.v for c in cases]), fl, n_phys=n_phys)
+        torch.cuda.synchronize()
+        assert m.n_virt == n_virt
+        np.testing.assert_array_equal(m.seg_table.cpu().numpy(), seg_o)
+        np.testing.assert_array_equal(m.kv_len.cpu().numpy(), kvl_o)
+        for layer, c in enumerate(cases):
+            _check_pool(c, seg_o[layer], fl, m.k_pool, m.v_pool)

@@ -159,3 +159,21 @@ def test_retrieval_edge_requests(dtype, P):
                     ctx_len=[500, 90, 1300, 7], q_len=[0, 90, 1, 3], policy=pol)
     print("case retrieval edges", dtype, P, flush=True)
     _run(c, importance_scores(c, levels=2))
+
+
+def test_retrieval_many_requests_and_selection_tasks():
+    # 200 requests with two retrieval heads each: more selection tasks than one launch holds
+    # (two selection launches) and more (request) groups than one scatter launch holds with a
+    # gather table per group (three scatter launches); heavily tied importance (4 levels) and
+    # long prefixes (up to 40K tokens, so the radix select's histogram passes are deep);
+    # kept lists, tables, pool rows and output against the oracle.
+    rng = np.random.default_rng(4242)
+    B = 200
+    ctx = [int(x) for x in rng.integers(1, 4000, B)]
+    ctx[0], ctx[1] = 40000, 25000
+    q = [min(c, int(rng.choice([1, 1, 3, 40]))) for c in ctx]
+    pol = [(RETRIEVAL, 4, 100), (GLOBAL, 0, 1), (RETRIEVAL, 0, 37), (LOCAL, 4, 256)]
+    c = custom_case(977, dtype="bf16", Hq=8, Hkv=4, D=64, P=64, ctx_len=ctx, q_len=q,
+                    policy=pol)
+    print("case retrieval many requests", flush=True)
+    _run(c, importance_scores(c, levels=4))
