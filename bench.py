@@ -407,7 +407,7 @@ def main() -> int:
                   "gbps_stream": round(build_bytes / (build_ms * 1e-3) / 1e9, 1)},
         "kv_savings": round(1.0 - rows / dense_tokens, 4),
         "parity_sample": {"rows": cpu_nrows, "max_abs": maxabs, "min_cos": cos_min},
-        "cpu_baseline": {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": threads,
+        "cpu_baseline": {"value": float("%.4g" % cpu_tflops), "unit": "TFLOP/s", "cores": threads,
                          "kind": "oracle",
                          "sample": "%d query rows (%d of %d (request, query head) pairs), "
                                    "fp64 numpy (%s BLAS), %.1f s; host has %d CPUs"
