@@ -179,6 +179,9 @@ def main() -> int:
                          "store them in profiles/counters.json (with the MFMA busy share, the "
                          "bf16 MFMA FLOPs per dispatch against the visible-pair FLOPs, and the "
                          "per-wave instruction counts per KV step)")
+    ap.add_argument("--counters-kernel", choices=("main", "build"), default="main",
+                    help="with --counters-from: the kernel whose dispatches are averaged (the "
+                         "workload's main attention kernel, or the build's scatter kernel)")
     ap.add_argument("--build-layers", type=int, default=0, metavar="N",
                     help="also time one build of N layers of this workload's shape into one "
                          "shared page pool (layer l's KV-head policies are the workload's "
@@ -608,7 +611,7 @@ def _main_kernel_counters(d: str, kernel: str) -> dict:
     vals = {}
     for r in csv.DictReader(open(files[0])):
         n = r["Kernel_Name"]
-        if kernel + "<" in n and ", 0>" in n:
+        if kernel + "<" in n and (kernel == "build_kernel" or ", 0>" in n):
             vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     if not vals:
         raise SystemExit("%s: no %s dispatch in %s" % (kernel, kernel, d))
@@ -623,18 +626,21 @@ def write_counters(args) -> int:
     case = config_case(args.config, with_tensors=False)
     decode = bool((case.q_len * (case.Hq // case.Hkv) <= 16).all())
     kernel = "decode_kernel" if decode else "prefill_kernel"
+    if args.counters_kernel == "build":
+        kernel = "build_kernel"
     counters = {}
     for d in args.counters_from:
         counters.update(_main_kernel_counters(d, kernel))
     rec = {"kernel": kernel, "counters": {k: round(v, 3) for k, v in sorted(counters.items())}}
     flops = 4.0 * case.D * visible_counts(case).sum() * (case.Hq // case.Hkv)
-    rec["visible_flops_per_launch"] = flops
-    if "MfmaFlopsBF16" in counters:
+    if kernel != "build_kernel":
+        rec["visible_flops_per_launch"] = flops
+    if "MfmaFlopsBF16" in counters and kernel != "build_kernel":
         rec["mfma_bf16_flops_per_launch"] = counters["MfmaFlopsBF16"]
         rec["mfma_flops_over_visible"] = round(counters["MfmaFlopsBF16"] / flops, 4)
     if "MfmaUtil" in counters:
         rec["mfma_busy_pct"] = round(counters["MfmaUtil"], 2)
-    if "SQ_WAVES" in counters and "SQ_INSTS_MFMA" in counters and not decode:
+    if "SQ_WAVES" in counters and "SQ_INSTS_MFMA" in counters and kernel == "prefill_kernel":
         # every prefill wave issues 32 bf16 MFMAs (32x32x16) per 64-key step
         steps = counters["SQ_INSTS_MFMA"] / 32.0
         rec["per_wave_step"] = {k[len("SQ_INSTS_"):].lower(): round(counters[k] / steps, 1)
