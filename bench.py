@@ -196,6 +196,10 @@ def main() -> int:
     ap.add_argument("--decode-requests", type=int, default=0, metavar="R",
                     help="with --decode-steps: only the workload's first R requests (a small "
                          "decode batch, where launch costs matter); 0 = all")
+    ap.add_argument("--page-order", choices=("shuffled", "sequential"), default="shuffled",
+                    help="order of the free list the build hands pages out from: a seeded "
+                         "permutation of the pool (default: pages scattered over the pool, as "
+                         "after allocator churn) or 0, 1, 2, ... (each segment's pages adjacent)")
     ap.add_argument("--gemm-reference", action="store_true",
                     help="only time torch's bf16 GEMM (hipBLASLt) at 4096^3..16384^3: what a "
                          "vendor-tuned dense contraction reaches on this GPU, for context")
@@ -215,7 +219,13 @@ def main() -> int:
 
     from head_aware_paged_segpaged_amd import (DenseMaskLayer, HipEvent, SegPagedDecoder,
                                                SegPagedLayer, SegPagedLayers)
-    from workloads import config_case, decode_tokens, free_list, importance_scores
+    from workloads import config_case, decode_tokens, importance_scores
+    from workloads import free_list as shuffled_free_list
+
+    def free_list(seed, n):
+        if args.page_order == "sequential":
+            return np.arange(n, dtype=np.int32)
+        return shuffled_free_list(seed, n)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
@@ -396,6 +406,7 @@ def main() -> int:
                    "local_window_rule": ("context length // %d" % int(case.policy[:, 2].max())
                                          if (case.policy[:, 0] == 2).any() else "fixed"),
                    "gqa_group": G,
+                   "page_order": args.page_order,
                    "retrieval_kv_heads": [[int(h), int(case.policy[h, 2])] for h in
                                           np.nonzero(case.policy[:, 0] == 3)[0]]},
         "gbps": round(gbps, 1),
@@ -424,7 +435,8 @@ def main() -> int:
     if args.build_layers > 0:
         del layer
         line["build_layers"] = build_layers_leg(args.build_layers, case, k, v, evict, stream,
-                                                SegPagedLayers, HipEvent, build_ms)
+                                                SegPagedLayers, HipEvent, build_ms,
+                                                sequential=args.page_order == "sequential")
     print(json.dumps(line), flush=True)
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -533,7 +545,7 @@ def decode_append_leg(args, case, k, v, up, evict, stream, planned_ms, decoder_c
 
 
 def build_layers_leg(n_layers, case, k, v, evict, stream, layers_cls, event_cls,
-                     one_layer_ms) -> dict:
+                     one_layer_ms, sequential=False) -> dict:
     """Median time of building ``n_layers`` layers of the workload's shape in one call into one
     shared pool: the stacked dense K/V are the workload's layer repeated (values do not change
     the build's work), the policies differ per layer."""
@@ -549,7 +561,8 @@ def build_layers_leg(n_layers, case, k, v, evict, stream, layers_cls, event_cls,
                 % (need / 2 ** 30, free / 2 ** 30)}
     kd = k.unsqueeze(0).expand(n_layers, *k.shape).contiguous()
     vd = v.unsqueeze(0).expand(n_layers, *v.shape).contiguous()
-    fl = np.random.default_rng(case.seed).permutation(max(layers.n_virt, 1)).astype(np.int32)
+    fl = (np.arange(max(layers.n_virt, 1), dtype=np.int32) if sequential else
+          np.random.default_rng(case.seed).permutation(max(layers.n_virt, 1)).astype(np.int32))
     layers.build(kd, vd, fl)
     walls, streams = [], []
     for _ in range(BUILD_RUNS):
@@ -647,6 +660,27 @@ def write_counters(args) -> int:
                                 for k in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
                                           "SQ_INSTS_MFMA", "SQ_INSTS_VALU_TRANS_F32")
                                 if k in counters}
+    if "GRBM_GUI_ACTIVE" in counters:
+        # GRBM_GUI_ACTIVE adds up the 8 XCDs' clocks; the _avr counters average over the
+        # block's instances, the _sum counters add them up (TD: one per CU, 256 CUs)
+        cyc = counters["GRBM_GUI_ACTIVE"] / 8.0
+        mp = {}
+        if "TA_BUSY_avr" in counters:
+            mp["ta_busy_pct"] = round(100.0 * counters["TA_BUSY_avr"] / cyc, 1)
+        if "TD_TD_BUSY_sum" in counters:
+            mp["td_busy_pct"] = round(100.0 * counters["TD_TD_BUSY_sum"] / 256.0 / cyc, 1)
+        if "TCC_BUSY_avr" in counters:
+            mp["l2_busy_pct"] = round(100.0 * counters["TCC_BUSY_avr"] / cyc, 1)
+        if "TCC_HIT_sum" in counters and "TCC_MISS_sum" in counters:
+            mp["l2_hit_pct"] = round(100.0 * counters["TCC_HIT_sum"] /
+                                     (counters["TCC_HIT_sum"] + counters["TCC_MISS_sum"]), 1)
+        if "TA_ADDR_STALLED_BY_TC_CYCLES_sum" in counters:
+            mp["ta_addr_stalled_by_l1_pct"] = round(
+                100.0 * counters["TA_ADDR_STALLED_BY_TC_CYCLES_sum"] / 256.0 / cyc, 1)
+        if "TCP_TCR_TCP_STALL_CYCLES_sum" in counters:
+            mp["l1_stalled_by_l2_pct"] = round(
+                100.0 * counters["TCP_TCR_TCP_STALL_CYCLES_sum"] / 256.0 / cyc, 1)
+        rec["memory_path"] = mp
     rec["source_hash"] = source_hash()
     path = os.path.join(ROOT, "profiles", "counters.json")
     data = json.load(open(path)) if os.path.exists(path) else {}

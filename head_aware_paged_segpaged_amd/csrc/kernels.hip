@@ -1480,13 +1480,14 @@ __global__ void __launch_bounds__(256) build_kernel(BuildParams p) {
     if (cb[mid] <= c) lo = mid; else hi = mid - 1;
   }
   const int g = lo, lc = c - cb[g];
-  // Head and segment of the group's chunk lc: lanes take heads lane and lane + 64, count
-  // their chunks (segment 0, then 1), and a prefix sum over the lanes orders them.
+  // Head and segment of the group's chunk lc: the wave takes the heads 64 at a time, lane l
+  // head 64 * r + l in round r, counts their chunks (segment 0, then 1), and a prefix sum
+  // over the lanes orders them.
   const int lane = __lane_id();
   const int32_t* rows = p.seg_table + int64_t(p.group0 + g) * p.Hkv * 8;
   int h = -1, s = 0, chunk = 0, base = 0;
-  for (int half = 0; half < 2 && h < 0; ++half) {
-    const int hh = lane + 64 * half;
+  for (int r = 0; r < (p.Hkv + 63) / 64 && h < 0; ++r) {
+    const int hh = lane + 64 * r;
     int n0 = 0, n1 = 0;
     if (hh < p.Hkv) {
       n0 = (rows[hh * 8 + 1] + kChunk - 1) / kChunk;
@@ -1511,7 +1512,7 @@ __global__ void __launch_bounds__(256) build_kernel(BuildParams p) {
     if (hit != 0) {
       const int l = int(__builtin_ctzll(hit));
       const int e = __shfl(excl, l), m0 = __shfl(n0, l);
-      h = l + 64 * half;
+      h = l + 64 * r;
       s = lc - e < m0 ? 0 : 1;
       chunk = lc - e - (s ? m0 : 0);
     }

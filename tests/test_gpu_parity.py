@@ -88,6 +88,14 @@ def _edge_cases():
         ("decode_g16", lambda: mk(31, dtype="bf16", Hq=16, Hkv=1, D=128, P=64,
                                   ctx_len=[5000, 63, 64, 65], q_len=[1, 1, 1, 1],
                                   policy=[(L_, 4, 512)])),
+        # more KV heads than one wave has lanes (the build enumerates heads 64 at a time)
+        ("kv_heads_200", lambda: mk(33, dtype="bf16", Hq=200, Hkv=200, D=64, P=16,
+                                    ctx_len=[150, 70, 300], q_len=[20, 1, 0],
+                                    policy=[(G_, 0, 1) if h % 7 == 0 else (L_, h % 5, 1 + h % 40)
+                                            for h in range(200)])),
+        # 32 query heads per KV head: a 128-row tile holds 4 query positions
+        ("gqa32", lambda: mk(34, dtype="bf16", Hq=64, Hkv=2, D=128, P=64, ctx_len=[700, 90],
+                             q_len=[50, 9], policy=[(L_, 4, 100), (G_, 0, 1)])),
         # windows that follow each request's context length: 450, 150, 1000 and 180, 60, 400
         ("adaptive_windows", lambda: mk(32, dtype="bf16", Hq=12, Hkv=3, D=128, P=64,
                                         ctx_len=[900, 300, 2000], q_len=[100, 1, 257],
