@@ -463,9 +463,8 @@ sp_status table_decode_shape(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
   *s = make_shape(kModePaged, dtype, B, Hq, Hkv, D, P, hint->data(), ones->data(), pol);
   sp_status st = check_shape(*s);
   if (st != SP_OK) return st;
-  // A decode item holds the G query heads of one KV head as its rows (at most kDecodeRows);
-  // larger groups would be planned as prefill items, which this call never launches.
-  if (Hq / Hkv > kDecodeRows) return SP_ERR_UNSUPPORTED;
+  // Groups of up to kDecodeRows query heads run as decode items (one wave each), larger ones
+  // (up to kTileRows, checked with the shape) as tiles of the prefill kernel.
   for (int32_t h = 0; h < Hkv; ++h)
     if (pol[h].kind == SP_LOCAL_ADAPTIVE) return SP_ERR_UNSUPPORTED;
   return SP_OK;
@@ -839,6 +838,14 @@ sp_status segpaged_decode(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, in
       n_phys < 1)
     return SP_ERR_INVALID_ARG;
   if (ws_bytes < size_t(kHeaderBytes)) return SP_ERR_WORKSPACE_TOO_SMALL;
+  // Every request has one query, so either every item is a decode item (G <= kDecodeRows) or
+  // every item is a tile of the prefill kernel; only that kernel is launched.
+  const bool tiles = Hq / Hkv > kDecodeRows;
+  // The prefill kernel with pages smaller than a KV step addresses rows from the pool start
+  // with 32-bit byte offsets.
+  if (tiles && page_size < kChunk &&
+      n_phys * int64_t(page_size) * D * (dtype == SP_BF16 ? 2 : 4) > int64_t(0x7fffffff))
+    return SP_ERR_UNSUPPORTED;
   int32_t gp = 0, gd = 0;
   st = grids(s, &gp, &gd);
   if (st != SP_OK) return st;
@@ -859,7 +866,8 @@ sp_status segpaged_decode(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, in
   p.G = s.Hq / s.Hkv;
   p.P = s.P;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
-  if (launch_attention(s.dtype, s.D, kModePaged, true, gd, p, stream) != hipSuccess)
+  if (launch_attention(s.dtype, s.D, kModePaged, !tiles, tiles ? gp : gd, p, stream) !=
+      hipSuccess)
     return SP_ERR_HIP;
   int cus = 0;
   st = device_cus(&cus);

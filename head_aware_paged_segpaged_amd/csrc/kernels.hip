@@ -649,6 +649,27 @@ __device__ __forceinline__ float keep_if(uint32_t bits, int c, float x) {
   return __uint_as_float((k & __float_as_uint(x)) | (~k & 0xff800000u));
 }
 
+// An item of a table-driven decode plan (ra_seg < 0) carries only its split: split c_begin of
+// c_end over all tokens its (request, KV head) stores, as the device tables hold them when the
+// kernel runs (segment 0, then segment 1). The query is the newest stored token: in decode the
+// request's last context position, which every head stores.
+__device__ __forceinline__ void table_item(WorkItem& w, ItemKV& kv) {
+  const int na = kv.ntok0, nb = kv.ntok1;
+  const int sa = (na + kChunk - 1) / kChunk, sb = (nb + kChunk - 1) / kChunk;
+  const int64_t n = sa + sb;
+  const int k = w.c_begin, ns = max(w.c_end, 1);
+  w.ra_seg = 0;
+  w.ra_begin = 0;
+  w.ra_end = na;
+  w.rb_seg = 1;
+  w.rb_begin = 0;
+  w.rb_end = nb;
+  w.c_begin = int(n * k / ns);
+  w.c_end = int(n * (k + 1) / ns);
+  w.p0 = (nb > 0 ? kv.pos1 + nb : kv.pos0 + na) - 1;
+  kv.n_ra = sa;
+}
+
 // ---------------------------------------------------------------------------------------
 // Prefill: persistent, 256 threads, 128-row tiles.
 // ---------------------------------------------------------------------------------------
@@ -718,9 +739,12 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     __syncthreads();
     const int it = uniform(s_item);
     if (it < 0) break;
-    const WorkItem w = load_item(items, it);
+    WorkItem w = load_item(items, it);
     ItemKV kv;
     load_item_kv(p, w, kDense, kv, p.ws);
+    if constexpr (!kDense) {
+      if (w.ra_seg < 0) table_item(w, kv);  // a decode query of more than 16 rows
+    }
     const int32_t* ph = pol + (w.b * p.Hkv + w.h) * 3;  // effective policy of (request, head)
     const int kind = uniform(ph[0]);
     const int sink = uniform(ph[1]);
@@ -1016,27 +1040,6 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
 // ---------------------------------------------------------------------------------------
 constexpr int kSub = 16;      // keys per decode sub-step
 constexpr int kDecAhead = 3;  // sub-steps of K and V in flight ahead of the one computed
-
-// A decode item of a table-driven plan (ra_seg < 0) carries only its split: split c_begin of
-// c_end over all tokens its (request, KV head) stores, as the device tables hold them when the
-// kernel runs (segment 0, then segment 1). The query is the newest stored token: in decode the
-// request's last context position, which every head stores.
-__device__ __forceinline__ void table_item(WorkItem& w, ItemKV& kv) {
-  const int na = kv.ntok0, nb = kv.ntok1;
-  const int sa = (na + kChunk - 1) / kChunk, sb = (nb + kChunk - 1) / kChunk;
-  const int64_t n = sa + sb;
-  const int k = w.c_begin, ns = max(w.c_end, 1);
-  w.ra_seg = 0;
-  w.ra_begin = 0;
-  w.ra_end = na;
-  w.rb_seg = 1;
-  w.rb_begin = 0;
-  w.rb_end = nb;
-  w.c_begin = int(n * k / ns);
-  w.c_end = int(n * (k + 1) / ns);
-  w.p0 = (nb > 0 ? kv.pos1 + nb : kv.pos0 + na) - 1;
-  kv.n_ra = sa;
-}
 
 // One decode sub-step: rows [vlo, vhi) of 16 are valid; `off` is the element offset of row 0
 // in the pool or the dense K/V (0 when there is no valid row).

@@ -473,17 +473,21 @@ sp_status make_plan(const Shape& s, int32_t slots_prefill, int32_t slots_decode,
   split_tiles(pre_tiles, slots_prefill, /*min_split=*/8, 0, &pre_items, &combine, &n_part_pre);
   split_tiles(dec_tiles, slots_decode, /*min_split=*/8, 1, &dec_items, &combine, &n_part_dec);
   if (table_decode) {
-    // Each decode item keeps only its split fraction (split c_begin of c_end); the kernel takes
-    // the head's stored tokens and query position from the device tables when it runs.
-    for (Tile& t : dec_items) {
-      WorkItem& w = t.w;
-      w.ra_seg = -1;
-      w.ra_begin = w.ra_end = 0;
-      w.rb_seg = 0;
-      w.rb_begin = w.rb_end = 0;
-      w.c_begin = t.split;
-      w.c_end = t.nsplit;
-      w.p0 = 0;
+    // Each item keeps only its split fraction (split c_begin of c_end); the kernel takes the
+    // head's stored tokens and query position from the device tables when it runs. Groups of
+    // up to kDecodeRows query heads are decode items; larger groups (one query, G rows) are
+    // tiles of the prefill kernel.
+    for (std::vector<Tile>* v : {&pre_items, &dec_items}) {
+      for (Tile& t : *v) {
+        WorkItem& w = t.w;
+        w.ra_seg = -1;
+        w.ra_begin = w.ra_end = 0;
+        w.rb_seg = 0;
+        w.rb_begin = w.rb_end = 0;
+        w.c_begin = t.split;
+        w.c_end = t.nsplit;
+        w.p0 = 0;
+      }
     }
   }
 

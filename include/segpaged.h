@@ -322,9 +322,9 @@ sp_status segpaged_append(sp_dtype dtype, int32_t B, int32_t Hkv, int32_t D, int
  * of a growing layout (and any layout segpaged_build writes). ctx_hint (host [B] >= 1, or NULL)
  * only sizes the KV splits; re-plan when the lengths have drifted far. The workspace, the
  * combine and reproducibility are as for segpaged_attention; errors likewise, plus
- * SP_ERR_UNSUPPORTED for SP_LOCAL_ADAPTIVE heads and for G = Hq / Hkv > 16 (a decode work item
- * holds the G query heads of one KV head, at most 16 rows; segpaged_attention with q_len 1
- * serves larger groups). */
+ * SP_ERR_UNSUPPORTED for SP_LOCAL_ADAPTIVE heads. Groups of G = Hq / Hkv <= 16 query heads run
+ * as decode items (one wave per item); larger groups (G <= 128) as 128-row tiles of the prefill
+ * kernel, one per (request, KV head, split), each reading the head's KV once for all G rows. */
 sp_status segpaged_decode_workspace_size(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv,
                                          int32_t D, int32_t page_size, const int32_t* ctx_hint,
                                          const sp_head_policy* pol, size_t* bytes);

@@ -283,21 +283,27 @@ def test_layers_build_rejects_retrieval_heads():
         binding.SP_ERR_INVALID_ARG
 
 
-def test_table_decode_rejects_groups_above_sixteen():
-    """A table-driven decode item holds the G query heads of one KV head as its rows, at most
-    16; a larger group is refused on the host (before any GPU call) instead of being planned
-    onto the prefill queue, which segpaged_decode never launches."""
+def test_table_decode_groups_up_to_128_query_heads():
+    """Groups of up to 16 query heads per KV head decode as one-wave items and larger ones (up to
+    128, a prefill tile's rows) as prefill tiles; a larger group is refused on the host, before
+    any GPU call."""
     pol = [(0, 0, 1)]
-    for Hq in (32, 64, 128):
-        with pytest.raises(sp.SegPagedError) as e:
-            sp.segpaged_decode_workspace_size("bf16", Hq, 1, 128, 64, [100, 200], pol)
-        assert e.value.status == binding.SP_ERR_UNSUPPORTED
+    for Hq in (16, 32, 64, 128):
+        # accepted: the size needs the device's CU count, so without a GPU the call gets as far
+        # as the HIP query
+        try:
+            assert sp.segpaged_decode_workspace_size("bf16", Hq, 1, 128, 64, [100, 200], pol) > 0
+        except sp.SegPagedError as e:
+            assert e.status == binding.SP_ERR_HIP
+    with pytest.raises(sp.SegPagedError) as e:
+        sp.segpaged_decode_workspace_size("bf16", 256, 1, 128, 64, [100, 200], pol)
+    assert e.value.status == binding.SP_ERR_UNSUPPORTED
     lib = binding.lib()
     fake = binding._vp(256)
     p = np.array(pol, np.int32)
-    st = lib.segpaged_decode(0, 2, 32, 1, 128, 64, binding._ptr(p), fake, fake, fake, 10, fake,
+    st = lib.segpaged_decode(0, 2, 256, 1, 128, 64, binding._ptr(p), fake, fake, fake, 10, fake,
                              fake, fake, 0.1, fake, fake, 1 << 20, None)
     assert st == binding.SP_ERR_UNSUPPORTED
-    st = lib.segpaged_decode_plan(0, 2, 32, 1, 128, 64, None, binding._ptr(p), fake, 1 << 20,
+    st = lib.segpaged_decode_plan(0, 2, 256, 1, 128, 64, None, binding._ptr(p), fake, 1 << 20,
                                   None)
     assert st == binding.SP_ERR_UNSUPPORTED

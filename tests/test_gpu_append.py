@@ -165,6 +165,15 @@ def test_append_with_retrieval_heads(P):
     _run(790 + P, "bf16", 8, 4, 128, P, [700, 2500, 90], [200, 1, 90], 60, pol)
 
 
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,P", [("bf16", 64, 2, 128, 64), ("bf16", 128, 1, 128, 16),
+                                              ("f32", 32, 1, 64, 32)])
+def test_append_with_large_query_groups(dtype, Hq, Hkv, D, P):
+    # more than 16 query heads per KV head: the table-driven decode runs the prefill kernel's
+    # tiles (all G rows of a (request, KV head) against its KV once per split)
+    pol = [(LOCAL, 4, 200), (GLOBAL, 0, 1)][:Hkv]
+    _run(760 + Hq + P, dtype, Hq, Hkv, D, P, [300, 2000, 90], [1, 50, 90], 40, pol)
+
+
 def test_append_long_ring_rotation():
     # A ring of 300 pages (window 4200, page 16, a 600-token prefill chunk): rotations go
     # through the three-reversal path; its first append drops 37 pages at once.
@@ -172,22 +181,25 @@ def test_append_long_ring_rotation():
          [(LOCAL, 0, 4200), (LOCAL, 8, 4100)], prefill_check=False)
 
 
-def test_table_decode_is_bitwise_the_planned_decode():
+@pytest.mark.parametrize("G", [4, 32])
+def test_table_decode_is_bitwise_the_planned_decode(G):
     # On a layout written by segpaged_build, the table-driven decode takes the same splits and
-    # ranges as the length-planned decode, so O is bitwise identical.
+    # ranges as the length-planned decode, so O is bitwise identical (G = 32: both run the
+    # prefill kernel's tiles).
     rng = np.random.default_rng(750)
     ctx = rng.integers(100, 9000, size=7)
     pol = [(GLOBAL, 0, 1), (LOCAL, 4, 512), (LOCAL, 0, 300), (GLOBAL, 0, 1),
            (LOCAL, 4, 2000), (LOCAL, 16, 64), (LOCAL, 4, 512), (LOCAL, 0, 5000)]
-    case = custom_case(751, dtype="bf16", Hq=32, Hkv=8, D=128, P=64, ctx_len=ctx,
+    Hq = 8 * G
+    case = custom_case(751, dtype="bf16", Hq=Hq, Hkv=8, D=128, P=64, ctx_len=ctx,
                        q_len=np.ones(7, dtype=np.int32), policy=pol)
-    print("case table-decode", ctx.tolist(), flush=True)
-    layer = SegPagedLayer("bf16", 32, 8, 128, 64, ctx, case.q_len, pol, DEV)
+    print("case table-decode G", G, ctx.tolist(), flush=True)
+    layer = SegPagedLayer("bf16", Hq, 8, 128, 64, ctx, case.q_len, pol, DEV)
     layer.build(to_device(case.k, "bf16"), to_device(case.v, "bf16"),
                 free_list(751, layer.n_virt))
     q = to_device(case.q, "bf16")
     a = layer.attention(q, case.scale)
-    dec = SegPagedDecoder("bf16", 32, 8, 128, 64, ctx, case.q_len, np.zeros(7), pol, DEV)
+    dec = SegPagedDecoder("bf16", Hq, 8, 128, 64, ctx, case.q_len, np.zeros(7), pol, DEV)
     dec.k_pool, dec.v_pool, dec.n_phys = layer.k_pool, layer.v_pool, layer.n_phys
     dec.seg_table, dec.kv_len, dec.v2p = layer.seg_table, layer.kv_len, layer.v2p
     b = dec.decode(q, case.scale)
@@ -265,21 +277,23 @@ def test_full_size_decode_append_all_rows(index):
     assert worst_abs <= MAXABS[c.dtype] and worst_cos > COS_MIN
 
 
-def test_decode_step_graph_replays_match_eager():
+@pytest.mark.parametrize("Hq", [16, 128])
+def test_decode_step_graph_replays_match_eager(Hq):
     # One decode step (append + table-driven decode) captured as a HIP graph and replayed with
     # new inputs copied into its buffers between replays, against the same steps run eagerly
-    # on an identical layout: every replay's output and tables bitwise equal.
+    # on an identical layout: every replay's output and tables bitwise equal (Hq = 128: 32
+    # query heads per KV head, the decode runs as prefill tiles).
     from workloads import decode_tokens
     pol = [(GLOBAL, 0, 1), (LOCAL, 0, 40), (LOCAL, 4, 100), (GLOBAL, 0, 1)]
     ctx, steps = np.array([300, 1200, 77]), 30
-    c = custom_case(780, dtype="bf16", Hq=16, Hkv=4, D=128, P=16, ctx_len=ctx, q_len=[1, 1, 1],
+    c = custom_case(780, dtype="bf16", Hq=Hq, Hkv=4, D=128, P=16, ctx_len=ctx, q_len=[1, 1, 1],
                     policy=pol)
-    print("case graph replay", flush=True)
+    print("case graph replay Hq", Hq, flush=True)
     kn, vn, qn = decode_tokens(c, steps)
     kd, vd, qd = to_device(kn, "bf16"), to_device(vn, "bf16"), to_device(qn, "bf16")
     decs = []
     for _ in range(2):
-        d = SegPagedDecoder("bf16", 16, 4, 128, 16, ctx, c.q_len, np.full(3, steps), pol, DEV)
+        d = SegPagedDecoder("bf16", Hq, 4, 128, 16, ctx, c.q_len, np.full(3, steps), pol, DEV)
         d.build(to_device(c.k, "bf16"), to_device(c.v, "bf16"), free_list(780, d.n_virt))
         d.plan()
         decs.append(d)
