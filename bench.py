@@ -251,7 +251,9 @@ def main() -> int:
     # kernels) on wall clock, and on HIP events around it on the stream.
     # RETRIEVAL heads keep the top fraction of their prefix by a seeded importance input
     importance = importance_scores(case) if (case.policy[:, 0] == 3).any() else None
-    layer.build(k, v, fl, importance=importance)
+    # the library takes importance head-major ([Hkv][T]); the oracle reads it token-major
+    layer.build(k, v, fl, importance=None if importance is None else
+                np.ascontiguousarray(importance.T))
     # Cache eviction between timed runs: READ a 512 MiB buffer that is never written. A
     # written buffer would leave dirty lines in the L2s and the MALL whose write-back then
     # lands inside the timed kernel (measured: a plain read kernel loses 11 % that way).
@@ -470,7 +472,8 @@ def decode_append_leg(args, case, k, v, up, evict, stream, planned_ms, decoder_c
     dec = decoder_cls(case.dtype, case.Hq, case.Hkv, case.D, case.P, ctx, ql, reserve,
                       case.policy, k.device)
     dec.build(k, v, free_list(case.seed, dec.n_virt),
-              importance=importance[:rows] if importance is not None else None)
+              importance=(np.ascontiguousarray(importance[:rows].T)
+                          if importance is not None else None))
     dec.plan()
     out = torch.empty_like(qn[0])
     local = case.policy[:, 0] == 1

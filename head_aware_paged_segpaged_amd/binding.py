@@ -272,7 +272,7 @@ def segpaged_retrieval_rows(ctx_len, q_len, policy) -> int:
 def segpaged_build_scored(dtype, D: int, page_size: int, ctx_len, q_len, policy, importance,
                           k_dense, v_dense, free_pages, n_phys: int, k_pool, v_pool, seg_table,
                           kv_len, v2p, row_pos, stream=None, reserve=None) -> None:
-    """importance: device float32 [sum(ctx_len)][Hkv]; row_pos: device int32 (or None);
+    """importance: device float32 [Hkv][sum(ctx_len)] (head-major); row_pos: device int32 (or None);
     reserve: host [B] (growable layout) or None."""
     c, q, p = _host_i32(ctx_len), _host_i32(q_len), _host_i32(policy).reshape(-1, 3)
     fl = _host_i32(free_pages)

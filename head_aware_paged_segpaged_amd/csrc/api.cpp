@@ -355,7 +355,7 @@ sp_status build_impl(sp_dtype dtype, int32_t n_layers, int32_t B, int32_t Hkv, i
     std::memset(&sp_, 0, sizeof(sp_));
     sp_.imp = importance;
     sp_.row_pos = row_pos;
-    sp_.Hkv = Hkv;
+    sp_.t_total = int32_t(t_total);
     for (size_t t0 = 0; t0 < tasks.size(); t0 += kMaxSelectTasks) {
       sp_.n_tasks = int32_t(std::min<size_t>(kMaxSelectTasks, tasks.size() - t0));
       std::memcpy(sp_.t, tasks.data() + t0, size_t(sp_.n_tasks) * sizeof(SelectTask));

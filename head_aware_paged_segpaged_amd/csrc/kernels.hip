@@ -1601,7 +1601,7 @@ __global__ void __launch_bounds__(kSelectThreads) select_kernel(SelectParams p) 
   int32_t* out = p.row_pos + t.out;
   for (int i = tid; i < t.sink; i += kSelectThreads) out[i] = i;
   if (t.k <= 0) return;
-  const float* col = p.imp + (int64_t(t.row0) + t.sink) * p.Hkv + t.h;  // candidate j: col[j * Hkv]
+  const float* col = p.imp + int64_t(t.h) * p.t_total + t.row0 + t.sink;  // candidate j: col[j]
   uint32_t prefix = 0, pmask = 0;
   int remaining = t.k;
 #pragma unroll 1
@@ -1617,7 +1617,7 @@ __global__ void __launch_bounds__(kSelectThreads) select_kernel(SelectParams p) 
 #pragma unroll
       for (int e = 0; e < kBatch; ++e) {
         const int j = j0 + e * kSelectThreads + tid;
-        key[e] = j < t.n ? order_key(col[int64_t(j) * p.Hkv]) : 0u;
+        key[e] = j < t.n ? order_key(col[j]) : 0u;
       }
 #pragma unroll
       for (int e = 0; e < kBatch; ++e) {
@@ -1669,7 +1669,7 @@ __global__ void __launch_bounds__(kSelectThreads) select_kernel(SelectParams p) 
     for (int e = 0; e < kPer; ++e) {
       const int j = j0 + kPer * tid + e;
       if (j < t.n) {
-        const uint32_t key = order_key(col[int64_t(j) * p.Hkv]);
+        const uint32_t key = order_key(col[j]);
         gt |= uint32_t(key > T) << e;
         eq |= uint32_t(key == T) << e;
       }

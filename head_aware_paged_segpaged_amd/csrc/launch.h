@@ -57,9 +57,9 @@ struct SelectTask {
 constexpr int kMaxSelectTasks = 160;
 
 struct SelectParams {
-  const float* imp;  // device [T][Hkv]
+  const float* imp;  // device [Hkv][T], T = rows of the dense K/V
   int32_t* row_pos;
-  int32_t Hkv, n_tasks;
+  int32_t t_total, n_tasks;
   SelectTask t[kMaxSelectTasks];
 };
 static_assert(sizeof(SelectParams) <= 4000, "selection arguments fit the kernel argument segment");

@@ -48,8 +48,9 @@ class SegPagedLayer:
     def build(self, k_dense: torch.Tensor, v_dense: torch.Tensor, free_pages,
               n_phys: int | None = None, stream=None, importance=None) -> None:
         """Allocate the pool and tables and fill them from dense [T, Hkv, D] K/V. Layouts with
-        RETRIEVAL heads need ``importance`` (float32 [T, Hkv], a device tensor or host array,
-        kept on the device for rebuilds)."""
+        RETRIEVAL heads need ``importance`` (float32 [Hkv, T], head-major: each KV head's
+        scores of all tokens contiguous; a device tensor or host array, kept on the device for
+        rebuilds)."""
         fl = np.asarray(free_pages, dtype=np.int32)
         self.n_phys = int(n_phys if n_phys is not None else max(self.n_virt, 1))
         t = _TORCH[self.dtype]
@@ -209,8 +210,8 @@ class SegPagedDecoder:
 
     def build(self, k_dense: torch.Tensor, v_dense: torch.Tensor, free_pages,
               n_phys: int | None = None, stream=None, importance=None) -> None:
-        """Layouts with RETRIEVAL heads need ``importance`` (float32 [T, Hkv], a device tensor
-        or host array)."""
+        """Layouts with RETRIEVAL heads need ``importance`` (float32 [Hkv, T], head-major; a
+        device tensor or host array)."""
         self.n_phys = int(n_phys if n_phys is not None else max(self.n_virt, 1))
         t = _TORCH[self.dtype]
         self.k_pool = torch.empty((max(self.n_phys, 1), self.P, self.D), dtype=t,

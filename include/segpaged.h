@@ -246,7 +246,8 @@ sp_status segpaged_retrieval_rows(int32_t B, const int32_t* ctx_len, const int32
  * plus:
  *   reserve    : host int32 [B] or NULL: with it the layout is the growable one of
  *                segpaged_build_growable (below), RETRIEVAL heads included
- *   importance : device float [sum(ctx_len)][Hkv], token-major like k_dense; only the prefix
+ *   importance : device float [Hkv][sum(ctx_len)], head-major (each head's scores of all
+ *                tokens contiguous, requests concatenated as in k_dense); only the prefix
  *                tokens of RETRIEVAL heads are read, on the device, by one selection work
  *                group per (request, retrieval head). The selection runs on a stream of the
  *                library's own (one per device, default priority, created on first use), forked

@@ -158,3 +158,8 @@ def group_parity(case, got: np.ndarray, groups, importance=None, q=None, k=None,
           % (case.name, label, rows, len(groups) * G, worst_abs, worst_cos, worst_at),
           flush=True)
     return worst_abs, worst_cos, rows
+
+
+def head_major(imp):
+    """The library's importance layout, [Hkv][T], from the workloads' token-major [T][Hkv]."""
+    return None if imp is None else np.ascontiguousarray(np.asarray(imp).T)

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from head_aware_paged_segpaged_amd import SP_ERR_SEGMENT_FULL, SegPagedDecoder, SegPagedLayer
-from tests.helpers import COS_MIN, DEV, MAXABS, group_parity, to_device, to_f64
+from tests.helpers import COS_MIN, DEV, MAXABS, group_parity, head_major, to_device, to_f64
 from workloads import GLOBAL, LOCAL, RETRIEVAL, custom_case, free_list, importance_scores
 
 pytestmark = pytest.mark.gpu
@@ -82,7 +82,7 @@ def _run(seed, dtype, Hq, Hkv, D, P, ctx, qb, steps, policy, mask_seed=None, pre
     n_phys = nv + 7
     fl = free_list(seed, n_phys)
     imp_build = _split_rows(imp, final, ctx) if retrieval else None
-    dec.build(k_build, v_build, fl, n_phys=n_phys, importance=imp_build)
+    dec.build(k_build, v_build, fl, n_phys=n_phys, importance=head_major(imp_build))
     v2p = fl[:nv].copy()
     keeps, row0 = {}, 0
     for b in range(len(ctx)):

@@ -336,7 +336,27 @@ def _adaptive_cases(n=6, seed=4048):
     return out
 
 
-@pytest.mark.parametrize("args", _random_cases() + _adaptive_cases(),
+def _large_group_cases(n=8, seed=8096):
+    """Random shapes with 12-64 query heads per KV head (prefill tiles of 2-10 query tokens,
+    decode queries as tiles), longer contexts and every page size."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([12, 24, 32, 64]))
+        B = int(rng.integers(1, 4))
+        ctx = rng.integers(1, 3000, B)
+        q = np.minimum(ctx, rng.choice([1, 7, 60], B))
+        pol = [(G_, 0, 1) if rng.random() < 0.4 else
+               (L_, int(rng.choice([0, 4, 64])), int(rng.choice([1, 50, 700])))
+               for _ in range(Hkv)]
+        out.append(dict(seed=700 + i, dtype="f32" if i == 7 else "bf16", Hq=Hkv * G, Hkv=Hkv,
+                        D=int(rng.choice([64, 128])), P=int(rng.choice([16, 32, 64, 256])),
+                        ctx_len=list(ctx), q_len=list(q), policy=pol))
+    return out
+
+
+@pytest.mark.parametrize("args", _random_cases() + _adaptive_cases() + _large_group_cases(),
                          ids=lambda a: "seed%d" % a["seed"])
 def test_random_shapes_against_oracle(args):
     # Seeded random shapes across dtypes, head dims, GQA groups, page sizes, request mixes

@@ -10,8 +10,8 @@ import torch
 import oracle
 from head_aware_paged_segpaged_amd import SegPagedLayer
 from head_aware_paged_segpaged_amd import binding as B
-from tests.helpers import (COS_MIN, DEV, MAXABS, assert_parity, group_parity, to_device,
-                           to_f64)
+from tests.helpers import (COS_MIN, DEV, MAXABS, assert_parity, group_parity, head_major,
+                           to_device, to_f64)
 from workloads import (GLOBAL, LOCAL, RETRIEVAL, config_case, custom_case, free_list,
                        importance_scores)
 
@@ -35,7 +35,7 @@ def _run(c, imp, n_phys=None):
     layer = SegPagedLayer(c.dtype, c.Hq, c.Hkv, c.D, c.P, c.ctx_len, c.q_len, c.policy, DEV)
     fl = free_list(c.seed, layer.n_virt if n_phys is None else n_phys)
     layer.build(to_device(c.k, c.dtype), to_device(c.v, c.dtype), fl, n_phys=n_phys,
-                importance=imp)
+                importance=head_major(imp))
     out = layer.attention(to_device(c.q, c.dtype), c.scale)
     torch.cuda.synchronize()
     assert layer.check() == 0
@@ -121,7 +121,8 @@ def test_full_size_retrieval_workload_all_rows():
     print("case full-size", c.name, flush=True)
     layer = SegPagedLayer(c.dtype, c.Hq, c.Hkv, c.D, c.P, c.ctx_len, c.q_len, c.policy, DEV)
     fl = free_list(c.seed, layer.n_virt)
-    layer.build(to_device(c.k, c.dtype), to_device(c.v, c.dtype), fl, importance=imp)
+    layer.build(to_device(c.k, c.dtype), to_device(c.v, c.dtype), fl,
+                importance=head_major(imp))
     out = to_f64(layer.attention(to_device(c.q, c.dtype), c.scale))
     torch.cuda.synchronize()
     assert layer.check() == 0
