@@ -102,8 +102,10 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_oracle_sample(case, budget_rows: int, importance=None):
-    """Times the fp64 oracle on a bounded sample of (request, query head) rows."""
+def cpu_oracle_sample(case, budget_rows: int, importance=None, budget_s: float = 0.0):
+    """Times the fp64 oracle on a bounded sample of (request, query head) rows: at most
+    budget_rows rows, and with budget_s > 0 it stops after the (request, query head) that takes
+    the time past budget_s."""
     import oracle
 
     rng = np.random.default_rng(1234)
@@ -125,11 +127,16 @@ def cpu_oracle_sample(case, budget_rows: int, importance=None):
         sample.append((b, hq, toks))
         rows += len(toks)
     t0 = time.perf_counter()
-    outs = [oracle.attention_rows(case.q, case.k, case.v, case.ctx_len, case.q_len, case.policy,
-                                  case.Hq, case.Hkv, case.scale, case.dtype, b, hq, toks,
-                                  importance=importance)
-            for b, hq, toks in sample]
+    outs = []
+    for b, hq, toks in sample:
+        outs.append(oracle.attention_rows(case.q, case.k, case.v, case.ctx_len, case.q_len,
+                                          case.policy, case.Hq, case.Hkv, case.scale, case.dtype,
+                                          b, hq, toks, importance=importance))
+        if budget_s > 0 and time.perf_counter() - t0 > budget_s:
+            break
     secs = time.perf_counter() - t0
+    sample = sample[:len(outs)]
+    rows = sum(len(t) for _, _, t in sample)
     # visible pairs of the sample
     G = case.Hq // case.Hkv
     pairs = 0.0
@@ -160,7 +167,8 @@ def main() -> int:
                          "Llama-3.3-70B-shaped layer (batch 4, 2048-token chunks of 16K-32K "
                          "contexts), the largest workload that runs on one GPU")
     ap.add_argument("--cpu-rows", type=int, default=None,
-                    help="rows of the CPU-oracle sample (default sized for about 10-30 s)")
+                    help="rows of the CPU-oracle sample (default: up to 64K rows spread over every "
+                         "(request, query head), stopping once about 15 s of oracle work is done)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense+mask timing")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps, each after reading a 512 MiB scratch buffer (evicts "
@@ -368,11 +376,12 @@ def main() -> int:
 
     # CPU oracle on a bounded sample, and parity of the sampled rows.
     threads = len(os.sched_getaffinity(0))
+    budget_s = 0.0
     if args.cpu_rows is None:
-        # the oracle converts one whole (request, KV head) to fp64 per sampled row set, so
-        # decode rows (one per head, contexts up to 128K) are far dearer than prefill rows
-        args.cpu_rows = 256 if int(case.q_len.max()) == 1 else 16384
-    sample, ref_rows, cpu_s, cpu_pairs, cpu_nrows = cpu_oracle_sample(case, args.cpu_rows, importance)
+        # about 15 s of oracle work: rows spread over every (request, query head), up to 64K
+        args.cpu_rows, budget_s = 65536, 15.0
+    sample, ref_rows, cpu_s, cpu_pairs, cpu_nrows = cpu_oracle_sample(case, args.cpu_rows,
+                                                                      importance, budget_s)
     got = out.float().cpu().numpy().astype(np.float64)
     q_row0 = np.concatenate([[0], np.cumsum(case.q_len)[:-1]])
     maxabs, cos_min = 0.0, 1.0
