@@ -1565,7 +1565,7 @@ __global__ void __launch_bounds__(256) build_kernel(BuildParams p) {
 // retrieval head) task writes the head's kept positions ascending: its sink, then the k most
 // important of the other n prefix tokens, ties going to the lower position. Importance values
 // map to unsigned keys in the same order; the k-th largest key T comes from a radix select
-// over three digits (12, 12 and 8 bits, one histogram pass each), then one pass in position
+// over three digits (10, 11 and 11 bits, one histogram pass each), then one pass in position
 // order takes every key above T and the first (k - count above T) keys equal to T.
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t order_key(float v) {
