@@ -961,8 +961,11 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
       F pb[2][16 / KPL];
       probs(sp0, sp1, mp, pb);
       pv(stg ? lv0 : lv1, pb);
-      if constexpr (kBf16)  // 32 scores per lane: 32 FMA + 16 packs + 16 dot2, 32 exponentials
-        step_schedule<2 * NQK, 48 / (2 * NQK), 32 / (2 * NQK), 4 * ND, 32 / (4 * ND), 4>();
+      // 32 scores per lane: 32 FMA + 16 packs + 16 dot2 and 32 exponentials; the exponentials
+      // and four VALU per S^T MFMA, the rest among the P*V MFMAs (measured best of the
+      // interleaves tried, by about 1 % over three VALU per S^T MFMA)
+      if constexpr (kBf16)
+        step_schedule<2 * NQK, 64 / (2 * NQK), 32 / (2 * NQK), 4 * ND, 16 / (4 * ND), 3>();
       mask(cur, sc0, sc1);
       mp = update_max(sc0, sc1);
       kv_barrier<0>();
