@@ -24,6 +24,15 @@ def _device_f32(x, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.float32))).to(device)
 
 
+def _check_importance(importance, Hkv: int, ctx_len) -> None:
+    """RETRIEVAL importance must be head-major, [Hkv, sum(ctx_len)]."""
+    shape = tuple(importance.shape)
+    want = (int(Hkv), int(np.asarray(ctx_len, dtype=np.int64).sum()))
+    if shape != want:
+        raise ValueError("importance must be [Hkv, sum(ctx_len)] = %s (head-major), got %s"
+                         % (want, shape))
+
+
 def _dt(dtype) -> str:
     return "bf16" if B._dtype_code(dtype) == B.SP_BF16 else "f32"
 
@@ -51,6 +60,8 @@ class SegPagedLayer:
         RETRIEVAL heads need ``importance`` (float32 [Hkv, T], head-major: each KV head's
         scores of all tokens contiguous; a device tensor or host array, kept on the device for
         rebuilds)."""
+        if importance is not None:
+            _check_importance(importance, self.Hkv, self.ctx_len)
         fl = np.asarray(free_pages, dtype=np.int32)
         self.n_phys = int(n_phys if n_phys is not None else max(self.n_virt, 1))
         t = _TORCH[self.dtype]
@@ -212,6 +223,8 @@ class SegPagedDecoder:
               n_phys: int | None = None, stream=None, importance=None) -> None:
         """Layouts with RETRIEVAL heads need ``importance`` (float32 [Hkv, T], head-major; a
         device tensor or host array)."""
+        if importance is not None:
+            _check_importance(importance, self.Hkv, self.ctx_len)
         self.n_phys = int(n_phys if n_phys is not None else max(self.n_virt, 1))
         t = _TORCH[self.dtype]
         self.k_pool = torch.empty((max(self.n_phys, 1), self.P, self.D), dtype=t,

@@ -307,3 +307,21 @@ def test_table_decode_groups_up_to_128_query_heads():
     st = lib.segpaged_decode_plan(0, 2, 256, 1, 128, 64, None, binding._ptr(p), fake, 1 << 20,
                                   None)
     assert st == binding.SP_ERR_UNSUPPORTED
+
+
+def test_runtime_rejects_token_major_importance():
+    """The library reads RETRIEVAL importance head-major, [Hkv][sum(ctx_len)]; the runtime
+    refuses any other shape before it allocates or calls the library."""
+    import torch
+
+    from head_aware_paged_segpaged_amd import SegPagedDecoder, SegPagedLayer
+    pol = [(3, 4, 100), (0, 0, 1), (1, 4, 32)]
+    ctx, q = [300, 50], [20, 1]
+    layer = SegPagedLayer("bf16", 6, 3, 64, 64, ctx, q, pol, "cpu")
+    dec = SegPagedDecoder("bf16", 6, 3, 64, 64, ctx, q, [4, 4], pol, "cpu")
+    k = torch.zeros((350, 3, 64), dtype=torch.bfloat16)
+    for bad in (np.zeros((350, 3), np.float32), np.zeros((3, 349), np.float32)):
+        with pytest.raises(ValueError):
+            layer.build(k, k, np.arange(layer.n_virt), importance=bad)
+        with pytest.raises(ValueError):
+            dec.build(k, k, np.arange(dec.n_virt), importance=bad)
