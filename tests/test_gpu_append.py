@@ -174,6 +174,37 @@ def test_append_with_large_query_groups(dtype, Hq, Hkv, D, P):
     _run(760 + Hq + P, dtype, Hq, Hkv, D, P, [300, 2000, 90], [1, 50, 90], 40, pol)
 
 
+def _growth_cases(n=64, seed=6060):
+    """Seeded random growth scenarios: GLOBAL, LOCAL and RETRIEVAL heads mixed, 1-32 query
+    heads per KV head, page sizes 16-256, idle requests on random steps."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        Hkv = int(rng.integers(1, 4))
+        G = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        B = int(rng.integers(1, 4))
+        ctx = [int(rng.integers(1, 2500)) for _ in range(B)]
+        qb = [min(c, int(rng.choice([1, 1, 5, 60]))) for c in ctx]
+        pol = []
+        for _ in range(Hkv):
+            r = rng.random()
+            pol.append((GLOBAL, 0, 1) if r < 0.3 else
+                       (LOCAL, int(rng.choice([0, 4, 40])), int(rng.choice([1, 30, 64, 300])))
+                       if r < 0.75 else (RETRIEVAL, int(rng.choice([0, 4])),
+                                         int(rng.choice([100, 500, 1000]))))
+        out.append((8000 + i, "f32" if i % 5 == 4 else "bf16", Hkv * G, Hkv,
+                    int(rng.choice([64, 128])), int(rng.choice([16, 32, 64, 256])), ctx, qb,
+                    int(rng.integers(3, 25)), pol, int(rng.integers(1, 99)) if i % 2 else None))
+    return out
+
+
+@pytest.mark.parametrize("args", _growth_cases(), ids=lambda a: "seed%d" % a[0])
+def test_random_growth_sweep(args):
+    seed, dtype, Hq, Hkv, D, P, ctx, qb, steps, pol, mask_seed = args
+    _run(seed, dtype, Hq, Hkv, D, P, ctx, qb, steps, pol, mask_seed=mask_seed,
+         prefill_check=seed % 3 == 0)
+
+
 def test_append_long_ring_rotation():
     # A ring of 300 pages (window 4200, page 16, a 600-token prefill chunk): rotations go
     # through the three-reversal path; its first append drops 37 pages at once.
