@@ -1467,7 +1467,8 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnParams p) {
 // positions from a list (a gather): layouts with such segments copy them in a launch of their
 // own (phase 2), after the selection that writes the list, and everything else before
 // (phase 1), so that the selection overlaps the bulk of the copy. Reads are whole D-rows,
-// writes whole contiguous page rows, both streaming (non-temporal): each byte is touched once.
+// streaming (non-temporal: each byte is read once); writes are whole contiguous page rows,
+// ordinary stores, which leave the caches free to gather the pages' lines before they go out.
 // ---------------------------------------------------------------------------------------
 template <class E, int D>
 __global__ void __launch_bounds__(256) build_kernel(BuildParams p) {
@@ -1557,8 +1558,8 @@ __global__ void __launch_bounds__(256) build_kernel(BuildParams p) {
   }
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) {
-    __builtin_nontemporal_store(kr[j], reinterpret_cast<u32x4_t*>(kp + dst[j]));
-    __builtin_nontemporal_store(vr[j], reinterpret_cast<u32x4_t*>(vp + dst[j]));
+    *reinterpret_cast<u32x4_t*>(kp + dst[j]) = kr[j];
+    *reinterpret_cast<u32x4_t*>(vp + dst[j]) = vr[j];
   }
 }
 
