@@ -142,32 +142,56 @@ __device__ __forceinline__ int wgs_on_xcd(int x) {
   return (int(gridDim.x) - x + kXcds - 1) / kXcds;
 }
 
+// The work queues as one work group sees them, read once when it starts: queue (xcd + k) %
+// kXcds at index k, its own XCD's first. In a one-round launch every queue fits the work groups
+// of its XCD, so each work group's first (static) pop is its only item and the queue counters
+// are never touched.
+struct Queues {
+  int32_t lo[kXcds], n[kXcds];  // first item and item count of queue (xcd + k) % kXcds
+  bool one_round;
+};
+
+__device__ __forceinline__ Queues load_queues(const int32_t* qb, int xcd) {
+  Queues q;
+  q.one_round = true;
+#pragma unroll
+  for (int k = 0; k < kXcds; ++k) {
+    const int x = (xcd + k) & (kXcds - 1);
+    q.lo[k] = qb[x];
+    q.n[k] = qb[x + 1] - qb[x];
+    q.one_round = q.one_round && q.n[k] <= wgs_on_xcd(x);
+  }
+  return q;
+}
+
 // Pops the next work item, one thread per work group. The first pop is static: the k-th work
 // group of an XCD takes item k of that XCD's queue, so the launch starts without a burst of
 // atomics on the queue counters. Later pops take the queue's counter (past the items handed
-// out statically): own XCD's queue first, then the others.
-__device__ __forceinline__ int pop_item(uint8_t* ws, const int32_t* qb, int cnt_off, int xcd,
+// out statically): own XCD's queue first, then the others. Bit k of `exhausted` marks queue
+// (xcd + k) % kXcds as empty.
+__device__ __forceinline__ int pop_item(uint8_t* ws, const Queues& q, int cnt_off, int xcd,
                                         uint32_t& exhausted, bool& first) {
   if (first) {
     first = false;
     const int k = int(blockIdx.x) / kXcds;
-    if (k < qb[xcd + 1] - qb[xcd]) return qb[xcd] + k;
+    if (k < q.n[0]) return q.lo[0] + k;
   }
+#pragma unroll
   for (int k = 0; k < kXcds; ++k) {
+    if (exhausted & (1u << k)) continue;
     const int x = (xcd + k) & (kXcds - 1);
-    if (exhausted & (1u << x)) continue;
-    const int n = qb[x + 1] - qb[x];
-    const int s = min(n, wgs_on_xcd(x));
-    if (n > s) {
+    const int s = min(q.n[k], wgs_on_xcd(x));
+    if (q.n[k] > s) {
       const int t = atomicAdd(reinterpret_cast<int*>(ws + cnt_off + x * 128), 1);
-      if (s + t < n) return qb[x] + s + t;
+      if (s + t < q.n[k]) return q.lo[k] + s + t;
     }
-    exhausted |= 1u << x;
+    exhausted |= 1u << k;
   }
   return -1;
 }
 
-// The last work group to finish returns the queue counters to zero for the next launch.
+// The last work group to finish returns the queue counters to zero for the next launch (not
+// called in one-round launches, which leave the counters at zero).
 __device__ __forceinline__ void retire(uint8_t* ws, int cnt_off, int done_off) {
   const int d = atomicAdd(reinterpret_cast<int*>(ws + done_off), 1);
   if (d == int(gridDim.x) - 1) {
@@ -708,6 +732,7 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
   const int lane = tid & 63;
   const int lq = lane & 31, hh = lane >> 5;
   const int xcd = blockIdx.x % kXcds;
+  const Queues queues = load_queues(hd->prefill_q, xcd);
   uint32_t exhausted = 0;
   bool first = true;
   const S* qbase = static_cast<const S*>(p.q);
@@ -735,7 +760,7 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
   for (int j = 0; j < 4; ++j) vo[j] = T::kFast && j < T::kLoads ? T::fast_voff(j) : 0u;
 
   for (;;) {
-    if (tid == 0) s_item = pop_item(p.ws, hd->prefill_q, kOffPrefillCnt, xcd, exhausted, first);
+    if (tid == 0) s_item = pop_item(p.ws, queues, kOffPrefillCnt, xcd, exhausted, first);
     __syncthreads();
     const int it = uniform(s_item);
     if (it < 0) break;
@@ -1027,7 +1052,7 @@ __global__ void __launch_bounds__(256, (sizeof(typename E::S) == 2 ? 2 : 1))
     }
     __syncthreads();
   }
-  if (tid == 0) retire(p.ws, kOffPrefillCnt, kOffPrefillDone);
+  if (tid == 0 && !queues.one_round) retire(p.ws, kOffPrefillCnt, kOffPrefillDone);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1157,6 +1182,7 @@ __global__ void __launch_bounds__(64) decode_kernel(AttnParams p) {
   const int lane = __lane_id();
   const int lc = lane & 15, k4 = lane >> 4;
   const int xcd = blockIdx.x % kXcds;
+  const Queues queues = load_queues(hd->decode_q, xcd);
   uint32_t exhausted = 0;
   bool first = true;
   const S* qbase = static_cast<const S*>(p.q);
@@ -1185,7 +1211,7 @@ __global__ void __launch_bounds__(64) decode_kernel(AttnParams p) {
 
   for (;;) {
     int it = 0;
-    if (lane == 0) it = pop_item(p.ws, hd->decode_q, kOffDecodeCnt, xcd, exhausted, first);
+    if (lane == 0) it = pop_item(p.ws, queues, kOffDecodeCnt, xcd, exhausted, first);
     it = uniform(it);
     if (it < 0) break;
     WorkItem w = load_item(items, it);
@@ -1362,7 +1388,7 @@ __global__ void __launch_bounds__(64) decode_kernel(AttnParams p) {
       }
     }
   }
-  if (lane == 0) retire(p.ws, kOffDecodeCnt, kOffDecodeDone);
+  if (lane == 0 && !queues.one_round) retire(p.ws, kOffDecodeCnt, kOffDecodeDone);
 }
 
 // ---------------------------------------------------------------------------------------
