@@ -96,27 +96,34 @@ sp_status workspace_size(const Shape& s, size_t* bytes) {
   return SP_OK;
 }
 
-// Combine items of recently planned shapes, by plan signature. segpaged_attention skips the
-// combine launch for a signature planned here with no KV-split item. The plan is a function
-// of what the signature hashes (shapes, lengths, policies, grid sizes), so an entry never goes
-// stale; a signature not found here (evicted, or planned in another process) launches the
+// Item counts of recently planned shapes, by plan signature. segpaged_attention skips the
+// combine launch for a signature planned here with no KV-split item, and sizes the decode grid
+// by its decode item count (see decode_grid). The plan is a function of what the signature
+// hashes (shapes, lengths, policies, grid sizes), so an entry never goes stale; a signature not
+// found here (evicted, or planned in another process) launches the full decode grid and the
 // combine, whose kernel reads the item count from the workspace and returns at once.
-class CombineCounts {
+class PlanCounts {
  public:
-  void put(uint64_t sig, int32_t n) {
+  struct Counts {
+    int32_t n_combine, n_decode;
+  };
+  void put(uint64_t sig, Counts c) {
     std::lock_guard<std::mutex> g(mu_);
     for (Entry& e : ent_)
       if (e.used && e.sig == sig) {
-        e.n = n;
+        e.c = c;
         return;
       }
-    ent_[next_] = Entry{sig, n, true};
+    ent_[next_] = Entry{sig, c, true};
     next_ = (next_ + 1) % kEntries;
   }
-  bool zero(uint64_t sig) {
+  bool get(uint64_t sig, Counts* c) {
     std::lock_guard<std::mutex> g(mu_);
     for (const Entry& e : ent_)
-      if (e.used && e.sig == sig) return e.n == 0;
+      if (e.used && e.sig == sig) {
+        *c = e.c;
+        return true;
+      }
     return false;
   }
 
@@ -124,7 +131,7 @@ class CombineCounts {
   static constexpr int kEntries = 64;
   struct Entry {
     uint64_t sig;
-    int32_t n;
+    Counts c;
     bool used;
   };
   std::mutex mu_;
@@ -132,9 +139,27 @@ class CombineCounts {
   int next_ = 0;
 };
 
-CombineCounts& combine_counts() {
-  static CombineCounts c;
+PlanCounts& plan_counts() {
+  static PlanCounts c;
   return c;
+}
+
+void remember_plan(const Plan& plan) {
+  plan_counts().put(plan.hdr.signature, PlanCounts::Counts{plan.hdr.n_combine, plan.hdr.n_decode});
+}
+
+// Work groups of a decode launch. The plan cuts decode items for gd slots (two one-wave work
+// groups per SIMD), and a launch with at most gd items runs them all at once. With more items
+// than that the launch has one work group per SIMD instead: the second wave of a SIMD gets its
+// issue slots only after the first (measured 1.5-2.5x slower per KV step), so a second wave
+// helps only while it has an item of its own, and the queues balance the rest.
+constexpr int32_t kSimdsPerCu = 4;  // CDNA compute units: four SIMDs each
+
+int32_t decode_grid(uint64_t sig, int32_t gd) {
+  PlanCounts::Counts c{0, 0};
+  int cus = 0;
+  if (!plan_counts().get(sig, &c) || c.n_decode <= gd || device_cus(&cus) != SP_OK) return gd;
+  return std::max<int32_t>(1, std::min<int32_t>(gd, cus * kSimdsPerCu));
 }
 
 sp_status plan_into(const Shape& s, void* workspace, size_t ws_bytes, hipStream_t stream) {
@@ -154,7 +179,7 @@ sp_status plan_into(const Shape& s, void* workspace, size_t ws_bytes, hipStream_
       hipSuccess)
     return SP_ERR_HIP;
   if (hipStreamSynchronize(stream) != hipSuccess) return SP_ERR_HIP;
-  combine_counts().put(plan.hdr.signature, plan.hdr.n_combine);
+  remember_plan(plan);
   return SP_OK;
 }
 
@@ -208,10 +233,12 @@ sp_status run_attention(const Shape& s, const void* q, const void* k, const void
   if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return SP_ERR_HIP;
   if (need_pre && launch_attention(s.dtype, s.D, s.mode, false, gp, p, stream) != hipSuccess)
     return SP_ERR_HIP;
-  if (need_dec && launch_attention(s.dtype, s.D, s.mode, true, gd, p, stream) != hipSuccess)
+  if (need_dec && launch_attention(s.dtype, s.D, s.mode, true, decode_grid(p.signature, gd), p,
+                                   stream) != hipSuccess)
     return SP_ERR_HIP;
   if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return SP_ERR_HIP;
-  if (combine_counts().zero(p.signature)) return SP_OK;
+  PlanCounts::Counts counts{0, 0};
+  if (plan_counts().get(p.signature, &counts) && counts.n_combine == 0) return SP_OK;
   int cus = 0;
   st = device_cus(&cus);
   if (st != SP_OK) return st;
@@ -688,7 +715,7 @@ sp_status segpaged_attention_static(sp_dtype dtype, int32_t B, int32_t Hq, int32
   if (hipMemcpyAsync(ws, buf.data(), buf.size(), hipMemcpyHostToDevice, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess)
     return SP_ERR_HIP;
-  combine_counts().put(plan.hdr.signature, plan.hdr.n_combine);
+  remember_plan(plan);
   st = run_attention(s, q, k_pool, v_pool, n_phys, seg_table, kv_len, v2p, softmax_scale, o, ws,
                      kStaticWorkspaceBytes, stream, nullptr, nullptr);
   if (st != SP_OK) return st;
@@ -817,6 +844,7 @@ sp_status segpaged_decode_plan(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hk
       hipSuccess)
     return SP_ERR_HIP;
   if (hipStreamSynchronize(stream) != hipSuccess) return SP_ERR_HIP;
+  remember_plan(plan);
   return SP_OK;
 }
 
@@ -866,8 +894,8 @@ sp_status segpaged_decode(sp_dtype dtype, int32_t B, int32_t Hq, int32_t Hkv, in
   p.G = s.Hq / s.Hkv;
   p.P = s.P;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
-  if (launch_attention(s.dtype, s.D, kModePaged, !tiles, tiles ? gp : gd, p, stream) !=
-      hipSuccess)
+  if (launch_attention(s.dtype, s.D, kModePaged, !tiles,
+                       tiles ? gp : decode_grid(p.signature, gd), p, stream) != hipSuccess)
     return SP_ERR_HIP;
   int cus = 0;
   st = device_cus(&cus);
