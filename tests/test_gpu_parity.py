@@ -243,6 +243,24 @@ def test_decode_repeat_is_bitwise_identical():
     assert layer.check() == 0
 
 
+@pytest.mark.parametrize("B", [2, 24, 44])
+def test_decode_launch_sizes(B):
+    # The decode kernel's launch size follows the plan's item count: on a 256-CU MI355X these
+    # batches plan 128, 1536 and 2112 decode items (bf16, D 128, 8 query heads per KV head), i.e.
+    # one work group per SIMD with every item started at once, the full grid of two per SIMD,
+    # and one per SIMD with the queues handing out the rest. Each must match the oracle, and
+    # repeated calls must give the same bits.
+    c = custom_case(4400 + B, dtype="bf16", Hq=64, Hkv=8, D=128, P=64, ctx_len=[4096] * B,
+                    q_len=[1] * B, policy=[(G_, 0, 1)] * 8)
+    print("case decode launch size", B, flush=True)
+    out, layer = run_segpaged(c)
+    assert_parity(to_f64(out), _oracle(c), c, "decode_launch_%d" % B)
+    o2 = layer.attention(to_device(c.q, c.dtype), c.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2)
+    assert layer.check() == 0
+
+
 @pytest.mark.parametrize("index", [2, 3, 4, 5, 6])
 def test_full_size_every_head(index):
     # The full workloads, planned for this device exactly as the benchmark runs them: page
